@@ -1,0 +1,65 @@
+"""Pins for the oracle's row expansion (CPU only)."""
+
+import numpy as np
+
+from oracle import rows
+from tests.conftest import load_golden
+
+
+def test_pages_worked_example_flattened():
+    g = load_golden("decode_expansion_worked_example.json")
+    got = rows.flattened_token_lengths(g["seq_lens"], g["decode_lens"])
+    assert got.tolist() == g["flattened_token_lengths"]
+    # context lengths = seq_len - decode_len, as the comment states
+    assert (np.array(g["seq_lens"]) - np.array(g["decode_lens"])).tolist() == g["context_lens"]
+
+
+def test_grid_rows_e4():
+    g = load_golden("e4_grid_rows.json")
+    L = rows.decode_lengths(g["seq_lens"], g["decode_lens"], g["next_n"])
+    assert L.tolist() == g["grid_lengths"]
+    q = rows.decode_query_rows(g["decode_lens"], g["next_n"], len(g["seq_lens"]), packed=True)
+    assert q.tolist() == g["packed_query_rows"]
+    # the grid keeps every real token's flattened length, in order
+    flat = rows.flattened_token_lengths(g["seq_lens"], g["decode_lens"])
+    assert L[L > 0].tolist() == flat.tolist()
+
+
+def test_uniform_grid_is_token_rows():
+    # full requests: both readings coincide with token_rows (mono runner page)
+    seq = [5, 100, 64, 65]
+    for q in (1, 2, 3):
+        L = rows.decode_lengths(seq, None, q)
+        assert L.tolist() == rows.token_rows(seq, q).tolist()
+        # and with the native-path formula seq - next_n + j + 1
+        assert L.tolist() == [s - q + j + 1 for s in seq for j in range(q)]
+
+
+def test_packed_mapping_brute_force():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        B = int(rng.integers(1, 9))
+        nn = int(rng.integers(1, 5))
+        dl = rng.integers(0, nn + 1, size=B)
+        q = rows.decode_query_rows(dl, nn, B, packed=True)
+        # enumerate the packed tokens as (request id, intra index) pairs
+        pairs = [(b, i) for b in range(B) for i in range(int(dl[b]))]
+        for t, (b, i) in enumerate(pairs):
+            assert q[b * nn + i] == t
+        assert (q >= 0).sum() == len(pairs)
+        qg = rows.decode_query_rows(dl, nn, B, packed=False)
+        for b in range(B):
+            for i in range(nn):
+                assert qg[b * nn + i] == (b * nn + i if i < dl[b] else -1)
+
+
+def test_prefill_rows_windows():
+    seq = [6, 4]
+    ql = [3, 2]
+    req, j, L, ks = rows.prefill_rows(seq, ql, 0, 2, 0, 5)
+    assert req.tolist() == [0, 0, 0, 1, 1]
+    assert j.tolist() == [0, 1, 2, 0, 1]
+    assert L.tolist() == [4, 5, 6, 3, 4]       # last query token sees every key
+    assert ks.tolist() == [0, 0, 0, 6, 6]
+    req, j, L, ks = rows.prefill_rows(seq, ql, 0, 2, 2, 4)
+    assert req.tolist() == [0, 1] and L.tolist() == [6, 3] and ks.tolist() == [0, 6]

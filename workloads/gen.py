@@ -1,0 +1,335 @@
+"""Seeded generators for the indexer workloads.
+
+Layout of the paged index cache (one reading of the pages, kept identical on
+both sides of the parity tests):
+
+* The cache is ``uint8[num_pages, page_bytes]``; page ``p`` holds
+  ``page_size`` (64) token rows back to back, token ``slot`` at byte
+  ``slot * row_bytes`` (token-major rows, as in the 3-D
+  ``(num_blocks, block_size, head_size)`` cache shape of the vLLM
+  DeepSeek-V3.2 indexer backend, ``get_kv_cache_shape``).
+* FP8 row: ``head_dim`` e4m3fn codes, then the fp32 per-token scale in 4
+  little-endian bytes (the "128 fp8 bytes and 4 scale bytes" entry noted in
+  ``get_max_prefill_buffer_size`` of that page).
+* MXFP4 row: ``head_dim/2`` bytes of packed e2m1 (element ``2j`` in the low
+  nibble of byte ``j``), then ``head_dim/32`` ue8m0 block scales (the
+  ``head_dim // 2 + head_dim // MXFP4_BLOCK_SIZE`` width of
+  ``kv_cache_as_quant_view`` on the glm5next sparse_indexer page).
+
+Key values are drawn N(0,1) and quantised here, once, when the inputs are
+made; the method itself only ever reads the quantised bytes.  Slots and
+pages that no request references are filled with 0xFF bytes ("poison": NaN
+codes / NaN scales) so that a read outside a request's live keys shows up as
+NaN in a checked output.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+PAGE_SIZE = 64
+FP8_MAX = 448.0
+POISON = 0xFF
+
+
+def row_bytes_for(fmt: str, head_dim: int) -> int:
+    """Bytes of one token row in the paged cache."""
+    if fmt == "fp8":
+        return head_dim + 4
+    if fmt == "mxfp4":
+        return head_dim // 2 + head_dim // 32
+    raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------
+# Encoders (input production only)
+# ----------------------------------------------------------------------------
+
+def encode_fp8_rows(k: np.ndarray) -> np.ndarray:
+    """fp32 keys [n, D] -> token rows [n, D+4]: e4m3fn codes at scale amax/448.
+
+    The code conversion is torch's float -> float8_e4m3fn cast (round to
+    nearest even) after clamping to the finite range.
+    """
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    n, d = k.shape
+    amax = np.abs(k).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    x = np.clip(k / scale[:, None], -FP8_MAX, FP8_MAX).astype(np.float32)
+    codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    out = np.empty((n, d + 4), dtype=np.uint8)
+    out[:, :d] = codes
+    out[:, d:] = scale.astype("<f4").view(np.uint8).reshape(n, 4)
+    return out
+
+
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def _e2m1_code(mag: np.ndarray) -> np.ndarray:
+    """Magnitudes (already divided by the block scale) -> 3-bit e2m1 codes,
+    round to nearest, ties to the even code, saturating at 6."""
+    mag = np.minimum(mag, 6.0)
+    # distance to every grid point; pick the nearest, ties -> even code
+    dist = np.abs(mag[..., None] - _E2M1_GRID)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    # prefer even code index among ties
+    even = cand & (np.arange(8) % 2 == 0)
+    pick_even = even.any(axis=-1)
+    code = np.where(pick_even, even.argmax(axis=-1), cand.argmax(axis=-1))
+    return code.astype(np.uint8)
+
+
+def encode_mxfp4_rows(k: np.ndarray) -> np.ndarray:
+    """fp32 keys [n, D] -> token rows [n, D/2 + D/32] in the OCP MX FP4 form:
+    per 32-element block a shared power-of-two scale 2^(floor(log2 amax) - 2),
+    elements rounded to e2m1 (nearest, ties to even, saturating)."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    n, d = k.shape
+    assert d % 32 == 0
+    nb = d // 32
+    blocks = k.reshape(n, nb, 32).astype(np.float64)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int32)
+    scaled = blocks / np.exp2(e.astype(np.float64))[..., None]
+    code = _e2m1_code(np.abs(scaled))
+    sign = (scaled < 0) & (code > 0)
+    nib = (code | (sign.astype(np.uint8) << 3)).reshape(n, d)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    out = np.empty((n, d // 2 + nb), dtype=np.uint8)
+    out[:, : d // 2] = packed
+    out[:, d // 2 :] = (e + 127).astype(np.uint8)
+    return out
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 (torch's round-to-nearest-even cast), returned as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+# ----------------------------------------------------------------------------
+# Workload container
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                     # "decode" | "prefill"
+    fmt: str                      # "fp8" | "mxfp4"
+    heads: int
+    head_dim: int
+    topk: int
+    page_size: int
+    page_bytes: int
+    cache: np.ndarray             # uint8 [num_pages, page_bytes]
+    block_table: np.ndarray       # int32 [num_req, width]
+    seq_lens: np.ndarray          # int32 [num_req]
+    q: np.ndarray                 # uint16 (bf16 bits) [rows, H, D]
+    w: np.ndarray                 # float32 [rows, H]
+    next_n: int = 1
+    decode_lens: np.ndarray | None = None   # int32 [num_req], decode only
+    q_packed: bool = False        # decode: q/w rows are packed tokens, not the grid
+    query_lens: np.ndarray | None = None    # int32 [num_req], prefill only
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_req(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.cache.shape[0])
+
+    @property
+    def row_bytes(self) -> int:
+        return row_bytes_for(self.fmt, self.head_dim)
+
+    @property
+    def grid_rows(self) -> int:
+        """Output rows: the padded [num_req, next_n] grid (decode) or every
+        query token (prefill)."""
+        if self.kind == "decode":
+            return self.num_req * self.next_n
+        return int(self.query_lens.sum())
+
+
+def _fill_cache(rng, fmt, head_dim, num_pages, page_bytes, block_table, seq_lens,
+                chunk_keys=1 << 18):
+    """Allocate the poisoned pool and write quantised N(0,1) keys into every
+    referenced slot (token t of request b -> page block_table[b, t//64],
+    slot t % 64).  Keys are drawn request by request, token order."""
+    rb = row_bytes_for(fmt, head_dim)
+    cache = np.full((num_pages, page_bytes), POISON, dtype=np.uint8)
+    enc = encode_fp8_rows if fmt == "fp8" else encode_mxfp4_rows
+    assert chunk_keys % PAGE_SIZE == 0
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        t0 = 0
+        while t0 < L:
+            t1 = min(L, t0 + chunk_keys)
+            rows = enc(rng.standard_normal((t1 - t0, head_dim), dtype=np.float32))
+            nfull = (t1 - t0) // PAGE_SIZE
+            if nfull:
+                pages = block_table[b, t0 // PAGE_SIZE : t0 // PAGE_SIZE + nfull]
+                cache[pages, : PAGE_SIZE * rb] = rows[: nfull * PAGE_SIZE].reshape(nfull, PAGE_SIZE * rb)
+            rest = (t1 - t0) - nfull * PAGE_SIZE
+            if rest:
+                page = block_table[b, t0 // PAGE_SIZE + nfull]
+                cache[page, : rest * rb] = rows[nfull * PAGE_SIZE :].reshape(-1)
+            t0 = t1
+    return cache
+
+
+def _deal_pages(rng, seq_lens, num_pages, width):
+    """Disjoint random pages for every request, dealt from one permutation of
+    the pool; unused table entries are 0 (as the pages' zero-filled tables)."""
+    need = [-(-int(L) // PAGE_SIZE) for L in seq_lens]
+    if sum(need) > num_pages:
+        raise ValueError("pool too small")
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.zeros((len(seq_lens), width), dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[pos : pos + n]
+        pos += n
+    return bt
+
+
+def build_decode(*, seed: int, seq_lens, heads: int, head_dim: int, topk: int,
+                 fmt: str = "fp8", next_n: int = 1, decode_lens=None,
+                 num_pages: int | None = None, pool_slack: float = 0.10,
+                 width: int | None = None, w_std: float | None = None,
+                 q_packed: bool = False, block_table=None, name: str = "decode",
+                 page_bytes: int | None = None) -> Workload:
+    """A decode batch: ``num_req`` requests, the padded [num_req, next_n] grid of
+    query rows.  Draw order after the lengths: block table, keys, q, w."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _build_decode_rng(rng, seq_lens=seq_lens, heads=heads, head_dim=head_dim,
+                             topk=topk, fmt=fmt, next_n=next_n, decode_lens=decode_lens,
+                             num_pages=num_pages, pool_slack=pool_slack, width=width,
+                             w_std=w_std, q_packed=q_packed, block_table=block_table,
+                             name=name, page_bytes=page_bytes)
+
+
+def _build_decode_rng(rng, *, seq_lens, heads, head_dim, topk, fmt, next_n, decode_lens,
+                      num_pages, pool_slack, width, w_std, q_packed, block_table, name,
+                      page_bytes):
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    if decode_lens is not None:
+        decode_lens = np.asarray(decode_lens, dtype=np.int32)
+    rb = row_bytes_for(fmt, head_dim)
+    pb = page_bytes if page_bytes is not None else PAGE_SIZE * rb
+    need_pages = sum(-(-int(L) // PAGE_SIZE) for L in seq_lens)
+    if num_pages is None:
+        num_pages = max(1, int(math.ceil(need_pages * (1.0 + pool_slack))))
+    if width is None:
+        width = max(1, -(-int(seq_lens.max(initial=1)) // PAGE_SIZE))
+    if block_table is None:
+        block_table = _deal_pages(rng, seq_lens, num_pages, width)
+    else:
+        block_table = np.asarray(block_table, dtype=np.int32)
+    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, block_table, seq_lens)
+    if q_packed:
+        rows = int(decode_lens.sum()) if decode_lens is not None else B * next_n
+    else:
+        rows = B * next_n
+    q32 = rng.standard_normal((rows, heads, head_dim), dtype=np.float32)
+    q = _bf16_bits(q32)
+    if w_std is None:
+        w_std = 1.0 / math.sqrt(heads)
+    w = (rng.standard_normal((rows, heads), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    return Workload(name=name, kind="decode", fmt=fmt, heads=heads, head_dim=head_dim,
+                    topk=topk, page_size=PAGE_SIZE, page_bytes=pb, cache=cache,
+                    block_table=block_table, seq_lens=seq_lens, q=q, w=w, next_n=next_n,
+                    decode_lens=decode_lens, q_packed=q_packed)
+
+
+def build_prefill(*, seed: int, seq_lens, query_lens, heads: int, head_dim: int,
+                  topk: int, fmt: str = "fp8", pool_slack: float = 0.10,
+                  w_std: float | None = None, name: str = "prefill") -> Workload:
+    """Prefill requests: request b has query_lens[b] query tokens, the last
+    ones of its seq_lens[b] keys.  q/w rows are every query token in order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    query_lens = np.asarray(query_lens, dtype=np.int32)
+    rb = row_bytes_for(fmt, head_dim)
+    pb = PAGE_SIZE * rb
+    need_pages = sum(-(-int(L) // PAGE_SIZE) for L in seq_lens)
+    num_pages = max(1, int(math.ceil(need_pages * (1.0 + pool_slack))))
+    width = max(1, -(-int(seq_lens.max(initial=1)) // PAGE_SIZE))
+    bt = _deal_pages(rng, seq_lens, num_pages, width)
+    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, bt, seq_lens)
+    rows = int(query_lens.sum())
+    q = _bf16_bits(rng.standard_normal((rows, heads, head_dim), dtype=np.float32))
+    if w_std is None:
+        w_std = 1.0 / math.sqrt(heads)
+    w = (rng.standard_normal((rows, heads), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    return Workload(name=name, kind="prefill", fmt=fmt, heads=heads, head_dim=head_dim,
+                    topk=topk, page_size=PAGE_SIZE, page_bytes=pb, cache=cache,
+                    block_table=bt, seq_lens=seq_lens, q=q, w=w, query_lens=query_lens)
+
+
+# ----------------------------------------------------------------------------
+# The five named workloads
+# ----------------------------------------------------------------------------
+
+CONFIG_NAMES = ("C1", "C2", "C3", "C4", "C5")
+
+
+def config(name: str) -> Workload:
+    """The five synthetic workloads, seeds 0..4.
+
+    C1 tiny decode: 1 request, L=300, 8-page pool whose block table is a
+       random permutation of the 8 pages; H=4, D=32, k=64.
+    C2 fp8 decode batch: 32 requests, L ~ U[4096, 32768], 20,000-page pool,
+       H=64, D=128, k=2048, w ~ N(0,1)/8.
+    C3 MTP non-uniform decode: 128 requests, decode_lens in {1,2} (p=1/2),
+       next_n=2 padded grid, L = floor(exp(U(ln 512, ln 131072))).
+    C4 MXFP4 long-context decode: 64 requests x L=131072, H=64, D=128, k=2048.
+    C5 chunked prefill: 2 requests, query 16384 of seq 65536 each.
+    """
+    if name == "C1":
+        rng = np.random.Generator(np.random.PCG64(0))
+        seq = np.array([300], dtype=np.int32)
+        perm = rng.permutation(8).astype(np.int32)[None, :]
+        wl = _build_decode_rng(rng, seq_lens=seq, heads=4, head_dim=32, topk=64, fmt="fp8",
+                               next_n=1, decode_lens=None, num_pages=8, pool_slack=0.0,
+                               width=8, w_std=0.5, q_packed=False, block_table=perm,
+                               name="C1", page_bytes=None)
+        return wl
+    if name == "C2":
+        rng = np.random.Generator(np.random.PCG64(1))
+        seq = rng.integers(4096, 32768, size=32, endpoint=True).astype(np.int32)
+        return _build_decode_rng(rng, seq_lens=seq, heads=64, head_dim=128, topk=2048, fmt="fp8",
+                                 next_n=1, decode_lens=None, num_pages=20000, pool_slack=0.0,
+                                 width=512, w_std=1.0 / 8, q_packed=False, block_table=None,
+                                 name="C2", page_bytes=None)
+    if name == "C3":
+        rng = np.random.Generator(np.random.PCG64(2))
+        dl = rng.integers(1, 2, size=128, endpoint=True).astype(np.int32)
+        seq = np.floor(np.exp(rng.uniform(math.log(512), math.log(131072), size=128))).astype(np.int32)
+        return _build_decode_rng(rng, seq_lens=seq, heads=64, head_dim=128, topk=2048, fmt="fp8",
+                                 next_n=2, decode_lens=dl, num_pages=None, pool_slack=0.10,
+                                 width=2048, w_std=1.0 / 8, q_packed=False, block_table=None,
+                                 name="C3", page_bytes=None)
+    if name == "C4":
+        rng = np.random.Generator(np.random.PCG64(3))
+        seq = np.full(64, 131072, dtype=np.int32)
+        return _build_decode_rng(rng, seq_lens=seq, heads=64, head_dim=128, topk=2048,
+                                 fmt="mxfp4", next_n=1, decode_lens=None, num_pages=None,
+                                 pool_slack=0.10, width=2048, w_std=1.0 / 8, q_packed=False,
+                                 block_table=None, name="C4", page_bytes=None)
+    if name == "C5":
+        return build_prefill(seed=4, seq_lens=[65536, 65536], query_lens=[16384, 16384],
+                             heads=64, head_dim=128, topk=2048, fmt="fp8", w_std=1.0 / 8,
+                             name="C5")
+    raise KeyError(name)
