@@ -1,0 +1,26 @@
+"""Sparse-attention lightning indexer for MI355X (gfx950).
+
+Paged fp8 / MXFP4 index-cache scoring and top-k selection, as a C-ABI HIP
+library (``libidx.so``, declared in ``include/idx.h``) with a thin ctypes
+binding.  PyTorch supplies device memory and streams only.
+"""
+
+from .binding import (  # noqa: F401
+    Cache,
+    IdxError,
+    Rows,
+    EXPORTED,
+    IDX_OP_DECODE_TOPK,
+    IDX_OP_LOGITS,
+    IDX_OP_TOPK,
+    IDX_DEV_BAD_PAGE,
+    idx_decode_topk,
+    idx_logits_paged,
+    idx_prefill_chunks,
+    idx_read_device_status,
+    idx_topk,
+    idx_version,
+    idx_workspace_bytes,
+    load,
+    new_workspace,
+)

@@ -1,0 +1,40 @@
+// Internal parameter blocks passed by value to the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace idx {
+
+// Limits of this build (checked on the host before any launch).
+constexpr int kMaxHeads = 64;
+constexpr int kMaxGroups = 4096;   // row groups per scorer launch (LDS table)
+constexpr int kMaxK = 4096;        // top-k
+constexpr int kMaxReqPrefill = 1024;
+constexpr int kStatusBytes = 256;  // workspace header (status word + pad)
+
+struct CacheArgs {
+  const uint8_t* base;
+  int64_t num_pages;
+  int64_t page_bytes;
+  int32_t head_dim;
+  int32_t row_bytes;
+  int32_t fmt;  // 0 fp8, 1 mxfp4
+};
+
+struct RowArgs {
+  int32_t kind;  // 0 decode, 1 prefill
+  int32_t num_req;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t max_len;
+  const int32_t* seq_lens;
+  const int32_t* decode_lens;
+  int32_t next_n;
+  int32_t q_packed;
+  const int32_t* qsl;
+  int32_t q_begin;
+  int32_t q_end;
+  int32_t num_rows;
+};
+
+}  // namespace idx

@@ -1,0 +1,332 @@
+// Host side of the indexer library: argument checks, workspace sizing,
+// kernel selection and launch.  See include/idx.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/idx.h"
+#include "idx_internal.h"
+#include "score.cuh"
+#include "topk.cuh"
+
+namespace idx {
+namespace {
+
+thread_local const char* g_last_error = "";
+
+// Records which check failed (for idx_last_error) and returns the status.
+idx_status fail(idx_status st, const char* what) {
+  g_last_error = what;
+  return st;
+}
+
+constexpr int kScoreThreads = 256;
+constexpr int kTopkThreads = 512;
+constexpr int kMinPagesPerBlock = 4;
+
+int row_bytes(int fmt, int d) { return fmt == IDX_FMT_FP8_E4M3 ? d + 4 : d / 2 + d / 32; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+idx_status check_cache(const idx_cache* c, CacheArgs& out) {
+  if (!c || !c->base) return fail(IDX_EINVAL, "cache descriptor or its base pointer is null");
+  if (c->num_pages <= 0 || c->page_bytes <= 0 || c->reserved != 0) return fail(IDX_EINVAL, "cache: num_pages and page_bytes must be positive, reserved 0");
+  if (c->page_size != kPage) return fail(IDX_EUNSUPPORTED, "cache: page_size must be 64");
+  if (c->fmt == IDX_FMT_FP8_E4M3) {
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return fail(IDX_EUNSUPPORTED, "cache: fp8 head_dim must be 32, 64 or 128");
+  } else if (c->fmt == IDX_FMT_MXFP4) {
+    if (c->head_dim != 128) return fail(IDX_EUNSUPPORTED, "cache: MXFP4 head_dim must be 128");
+  } else {
+    return fail(IDX_EUNSUPPORTED, "cache: unknown format");
+  }
+  const int rb = row_bytes(c->fmt, c->head_dim);
+  if (c->page_bytes < static_cast<int64_t>(kPage) * rb) return fail(IDX_EINVAL, "cache: page_bytes smaller than 64 token rows");
+  if ((c->page_bytes & 15) != 0 || (reinterpret_cast<uintptr_t>(c->base) & 15) != 0) return fail(IDX_EINVAL, "cache: base and page_bytes must be 16-byte aligned");
+  out.base = static_cast<const uint8_t*>(c->base);
+  out.num_pages = c->num_pages;
+  out.page_bytes = c->page_bytes;
+  out.head_dim = c->head_dim;
+  out.row_bytes = rb;
+  out.fmt = c->fmt;
+  return IDX_OK;
+}
+
+int64_t rows_count(const idx_rows* r) {
+  if (!r) return -1;
+  if (r->kind == IDX_ROWS_DECODE) {
+    if (r->num_req < 0 || r->next_n < 1) return -1;
+    return static_cast<int64_t>(r->num_req) * r->next_n;
+  }
+  if (r->kind == IDX_ROWS_PREFILL) {
+    if (r->q_begin < 0 || r->q_end < r->q_begin) return -1;
+    return static_cast<int64_t>(r->q_end) - r->q_begin;
+  }
+  return -1;
+}
+
+// `need_table`: the block table is read (scoring); top-k needs lengths only.
+idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
+  const int64_t nrows = rows_count(r);
+  if (nrows < 0) return fail(IDX_EINVAL, "rows: bad kind, next_n < 1 or q_end < q_begin");
+  if (r->num_req < 0 || r->max_seq_len < 0) return fail(IDX_EINVAL, "rows: negative num_req or max_seq_len");
+  if (r->num_req > 0 && !r->seq_lens) return fail(IDX_EINVAL, "rows: seq_lens is null");
+  if (need_table) {
+    if (r->num_req > 0 && !r->block_table) return fail(IDX_EINVAL, "rows: block_table is null");
+    if (r->bt_width < 0 || r->bt_stride < r->bt_width) return fail(IDX_EINVAL, "rows: bt_stride < bt_width");
+    if (static_cast<int64_t>(r->max_seq_len) > static_cast<int64_t>(r->bt_width) * kPage) return fail(IDX_EINVAL, "rows: max_seq_len exceeds bt_width * 64");
+  }
+  if (nrows > (int64_t{1} << 30)) return fail(IDX_EUNSUPPORTED, "rows: more than 2^30 rows");
+  if (r->kind == IDX_ROWS_DECODE) {
+    if (r->q_packed != 0 && r->q_packed != 1) return fail(IDX_EINVAL, "rows: q_packed must be 0 or 1");
+    if (r->q_packed && r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: packed queries support at most 1024 requests");
+  } else {
+    if (r->num_req > 0 && !r->query_start_loc) return fail(IDX_EINVAL, "rows: query_start_loc is null");
+    if (r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: a prefill chunk supports at most 1024 requests");
+    if (r->num_req == 0 && nrows > 0) return fail(IDX_EINVAL, "rows: prefill rows without requests");
+  }
+  out.kind = r->kind;
+  out.num_req = r->num_req;
+  out.block_table = r->block_table;
+  out.bt_stride = r->bt_stride;
+  out.max_len = r->max_seq_len;
+  out.seq_lens = r->seq_lens;
+  out.decode_lens = r->decode_lens;
+  out.next_n = r->kind == IDX_ROWS_DECODE ? r->next_n : 1;
+  out.q_packed = r->kind == IDX_ROWS_DECODE ? r->q_packed : 0;
+  out.qsl = r->query_start_loc;
+  out.q_begin = r->q_begin;
+  out.q_end = r->q_end;
+  out.num_rows = static_cast<int32_t>(nrows);
+  return IDX_OK;
+}
+
+int pick_rg(const RowArgs& R) { return (R.kind == 0 && R.next_n == 1) ? 1 : 2; }
+
+// Upper bound of the scorer's row groups.
+int64_t group_bound(const RowArgs& R, int rg) {
+  if (R.kind == 0) return static_cast<int64_t>(R.num_req) * ceil_div(R.next_n, rg);
+  return ceil_div(R.num_rows, rg) + R.num_req;
+}
+
+int64_t scratch_stride(const RowArgs& R) {
+  const int64_t m = R.max_len > 0 ? R.max_len : 1;
+  return ceil_div(m, 64) * 64;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Decode-topk workspace: [status 256 B][counters][scratch logits]
+size_t counters_offset() { return kStatusBytes; }
+size_t scratch_offset(const RowArgs& R, int rg) {
+  return align_up(counters_offset() + sizeof(int32_t) * static_cast<size_t>(group_bound(R, rg)), 256);
+}
+size_t decode_ws_bytes(const RowArgs& R, int rg) {
+  return scratch_offset(R, rg) + sizeof(float) * static_cast<size_t>(R.num_rows) * scratch_stride(R);
+}
+
+template <int D, bool MX, int RG, int MT, bool F>
+hipError_t launch_score(const ScoreParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((score_kernel<D, MX, RG, MT, F>), dim3(grid), dim3(kScoreThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool F>
+hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s) {
+  const int d = p.cache.head_dim;
+  const bool mx = p.cache.fmt == IDX_FMT_MXFP4;
+  const int mt = p.heads > 32 ? 2 : 1;
+#define IDX_SCORE_CASE(D_, MX_, RG_, MT_) \
+  if (d == D_ && mx == MX_ && rg == RG_ && mt == MT_) return launch_score<D_, MX_, RG_, MT_, F>(p, grid, s);
+#define IDX_SCORE_RGMT(D_, MX_) \
+  IDX_SCORE_CASE(D_, MX_, 1, 1) IDX_SCORE_CASE(D_, MX_, 1, 2) IDX_SCORE_CASE(D_, MX_, 2, 1) IDX_SCORE_CASE(D_, MX_, 2, 2)
+  IDX_SCORE_RGMT(128, false)
+  IDX_SCORE_RGMT(64, false)
+  IDX_SCORE_RGMT(32, false)
+  IDX_SCORE_RGMT(128, true)
+#undef IDX_SCORE_RGMT
+#undef IDX_SCORE_CASE
+  return hipErrorInvalidValue;
+}
+
+int score_grid(const RowArgs& R, int rg) {
+  const int64_t pages = group_bound(R, rg) * ceil_div(R.max_len, kPage);
+  int64_t g = ceil_div(pages, kMinPagesPerBlock);
+  const int64_t gmax = static_cast<int64_t>(device_cu_count()) * 2;
+  if (g > gmax) g = gmax;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+idx_status check_queries(const uint16_t* q, const float* w, int heads) {
+  if (heads < 1) return fail(IDX_EINVAL, "heads must be >= 1");
+  if (heads > kMaxHeads) return fail(IDX_EUNSUPPORTED, "heads must be <= 64");
+  if (!q || !w) return fail(IDX_EINVAL, "q or w is null");
+  if ((reinterpret_cast<uintptr_t>(q) & 15) != 0) return fail(IDX_EINVAL, "q must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(w) & 3) != 0) return fail(IDX_EINVAL, "w must be 4-byte aligned");
+  return IDX_OK;
+}
+
+idx_status check_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return fail(IDX_EINVAL, "workspace is null");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(IDX_EINVAL, "workspace must be 256-byte aligned");
+  if (have < need) return fail(IDX_ENOSPC, "workspace too small (see idx_workspace_bytes)");
+  return IDX_OK;
+}
+
+}  // namespace
+}  // namespace idx
+
+using namespace idx;
+
+extern "C" {
+
+int64_t idx_num_rows(const idx_rows* rows) { return rows_count(rows); }
+
+size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* rows, int32_t heads,
+                           int32_t k) {
+  RowArgs R;
+  if (op == IDX_OP_TOPK) {
+    if (check_rows(rows, false, R) != IDX_OK) return 0;
+    return kStatusBytes;
+  }
+  CacheArgs C;
+  if (check_cache(cache, C) != IDX_OK || check_rows(rows, true, R) != IDX_OK) return 0;
+  if (heads < 1 || heads > kMaxHeads) return 0;
+  if (op == IDX_OP_LOGITS) return kStatusBytes;
+  if (op == IDX_OP_DECODE_TOPK) {
+    if (R.kind != IDX_ROWS_DECODE || k < 1 || k > kMaxK) return 0;
+    return decode_ws_bytes(R, pick_rg(R));
+  }
+  return 0;
+}
+
+idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
+                            const float* w, int32_t heads, float* logits, int64_t logits_stride,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  CacheArgs C;
+  RowArgs R;
+  idx_status st = check_cache(cache, C);
+  if (st != IDX_OK) return st;
+  if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
+  if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
+  if (!logits || logits_stride < 0) return fail(IDX_EINVAL, "logits is null or logits_stride < 0");
+  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
+  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
+  const int rg = pick_rg(R);
+  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 4096)");
+  if (R.num_rows == 0 || R.max_len == 0) return IDX_OK;
+  ScoreParams p{};
+  p.cache = C;
+  p.rows = R;
+  p.q = q;
+  p.w = w;
+  p.heads = heads;
+  p.k = 0;
+  p.logits = logits;
+  p.logits_stride = logits_stride;
+  p.status = static_cast<uint32_t*>(workspace);
+  p.num_groups = static_cast<int32_t>(group_bound(R, rg));
+  const hipError_t e = dispatch_score<false>(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+}
+
+idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, int32_t k,
+                    int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  RowArgs R;
+  idx_status st = check_rows(rows, false, R);
+  if (st != IDX_OK) return st;
+  if (!logits || !out || logits_stride < 0) return fail(IDX_EINVAL, "logits or out is null, or logits_stride < 0");
+  if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
+  if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
+  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
+  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
+  if (R.num_rows == 0) return IDX_OK;
+  TopkParams p{};
+  p.logits = logits;
+  p.stride = logits_stride;
+  p.rows = R;
+  p.k = k;
+  p.out = out;
+  hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+}
+
+idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
+                           const float* w, int32_t heads, int32_t k, int32_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  CacheArgs C;
+  RowArgs R;
+  idx_status st = check_cache(cache, C);
+  if (st != IDX_OK) return st;
+  if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
+  if (R.kind != IDX_ROWS_DECODE) return fail(IDX_EINVAL, "idx_decode_topk takes DECODE rows");
+  if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
+  if (!out) return fail(IDX_EINVAL, "out is null");
+  if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
+  if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
+  const int rg = pick_rg(R);
+  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 4096)");
+  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R, rg))) != IDX_OK) return st;
+  if (R.num_rows == 0) return IDX_OK;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  ScoreParams p{};
+  p.cache = C;
+  p.rows = R;
+  p.q = q;
+  p.w = w;
+  p.heads = heads;
+  p.k = k;
+  p.logits = reinterpret_cast<float*>(ws + scratch_offset(R, rg));
+  p.logits_stride = scratch_stride(R);
+  p.out = out;
+  p.counters = reinterpret_cast<int32_t*>(ws + counters_offset());
+  p.status = reinterpret_cast<uint32_t*>(ws);
+  p.num_groups = static_cast<int32_t>(group_bound(R, rg));
+  const hipError_t e = dispatch_score<true>(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+}
+
+idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return fail(IDX_EINVAL, "workspace or flags is null");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return fail(IDX_EHIP, "reading the status word failed");
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(IDX_EHIP, "stream synchronisation failed");
+  *flags = v;
+  const uint32_t zero = 0;
+  if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess) return fail(IDX_EHIP, "clearing the status word failed");
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(IDX_EHIP, "stream synchronisation failed");
+  return IDX_OK;
+}
+
+const char* idx_status_string(idx_status s) {
+  switch (s) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported shape or format";
+    case IDX_ENOSPC: return "workspace or output capacity too small";
+    case IDX_EHIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* idx_version(void) { return "0.1.0"; }
+
+const char* idx_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -236,7 +236,7 @@ def _build_decode_rng(rng, *, seq_lens, heads, head_dim, topk, fmt, next_n, deco
     if block_table is None:
         block_table = _deal_pages(rng, seq_lens, num_pages, width)
     else:
-        block_table = np.asarray(block_table, dtype=np.int32)
+        block_table = np.array(block_table, dtype=np.int32, order="C", copy=True)
     cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, block_table, seq_lens)
     if q_packed:
         rows = int(decode_lens.sum()) if decode_lens is not None else B * next_n
@@ -300,7 +300,7 @@ def config(name: str) -> Workload:
     if name == "C1":
         rng = np.random.Generator(np.random.PCG64(0))
         seq = np.array([300], dtype=np.int32)
-        perm = rng.permutation(8).astype(np.int32)[None, :]
+        perm = rng.permutation(8).astype(np.int32).reshape(1, 8).copy()
         wl = _build_decode_rng(rng, seq_lens=seq, heads=4, head_dim=32, topk=64, fmt="fp8",
                                next_n=1, decode_lens=None, num_pages=8, pool_slack=0.0,
                                width=8, w_std=0.5, q_packed=False, block_table=perm,
