@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode indexer (scoring + top-k) on one MI355X.
+
+Workload: the fp8 decode batch -- 32 requests, seq_len ~ U[4096, 32768],
+page 64, 20,000-page pool, H=64 index heads, head_dim 128, top-k 2048,
+next_n=1 (synthetic, seeded).  A step is one idx_decode_topk call over the
+whole batch: row expansion, page gather, bf16-MFMA scoring with the
+ReLU-weighted head sum, and the fused top-k.
+
+Timing: inputs are resident in HBM before the timed region.  The pool
+(169 MB) would fit the 256 MiB MALL, so each step reads one of `--copies`
+identical pools in rotation (8 x 169 MB by default); between two uses of a
+pool ~550 MB of other keys stream through, so the keys come from HBM.  K
+steps are bracketed by synchronisation; HIP events on the launch stream
+give the per-launch duration used for the roofline.
+
+Prints one JSON line.  `--summarize-prof DIR...` turns rocprofv3 outputs
+(kernel-trace stats and FETCH_SIZE / WRITE_SIZE counter runs) into
+profiles/decode_fused_fp8_c2.{md,json}, which later runs use for `traffic`.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "index keys scored/sec + top-k rows/sec, 1×MI355X; % of HBM (decode) / MFMA (prefill) peak"
+HBM_PEAK_GBS = 8000.0
+PROFILE_NAME = "decode_fused_fp8_c2"
+KERNEL_SUBSTR = "score_kernelILi128ELb0ELi1ELi2ELb1E"   # fused decode, D=128, fp8, 1 row/group, 64 heads
+CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes one fused decode launch must move at minimum: every live key
+    row once (D codes + 4-byte scale), each row's bf16 q and fp32 w, the
+    block-table entries of the live pages, the lengths, and the top-k out."""
+    keys = int(wl.seq_lens.astype("int64").sum())
+    rows = wl.num_req * wl.next_n
+    pages = int(sum(-(-int(L) // 64) for L in wl.seq_lens))
+    b = {
+        "keys": keys * wl.row_bytes,
+        "q": rows * wl.heads * wl.head_dim * 2,
+        "w": rows * wl.heads * 4,
+        "block_table": pages * 4,
+        "lengths": wl.num_req * 4,
+        "out": rows * wl.topk * 4,
+    }
+    b["total"] = sum(b.values())
+    return b
+
+
+def scored_keys(wl) -> int:
+    """Keys the fused decode scores: sum of L over grid rows with L > k
+    (shorter rows are causal-filled without scoring)."""
+    total = 0
+    for b in range(wl.num_req):
+        dl = wl.next_n if wl.decode_lens is None else int(wl.decode_lens[b])
+        for i in range(min(dl, wl.next_n)):
+            L = int(wl.seq_lens[b]) - dl + i + 1
+            total += L if L > wl.topk else 0
+    return total
+
+
+def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
+    """The oracle (numpy, float64) on the host cores, on as many whole
+    requests as fit in about `budget_s` seconds."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    keys = 0
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(wl.num_req):
+        lg = oracle.pipeline.decode_logits(wl, requests=[b])
+        oracle.pipeline.decode_topk(wl, lg, requests=[b])
+        keys += int(sum(len(v) for v in lg.values() if len(v) > wl.topk))
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": keys / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {wl.num_req} requests ({keys} keys, {dt:.1f} s), logits + top-k, "
+                      f"cpus visible {len(os.sched_getaffinity(0))}"}
+
+
+def load_traffic(per_launch_bytes: int):
+    path = os.path.join(ROOT, "profiles", PROFILE_NAME + ".json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        prof = json.load(f)
+    if prof.get("source_hash") != kernel_source_hash():
+        return None, prof
+    t = prof.get("traffic_bytes_per_launch")
+    return t, prof
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_decode_amd as idx
+    from workloads import config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = config(args.config)
+    pools = [torch.from_numpy(wl.cache).to(dev)]
+    for _ in range(args.copies - 1):
+        pools.append(pools[0].clone())
+    caches = [idx.Cache(p, wl.head_dim, wl.fmt) for p in pools]
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    seq = torch.from_numpy(wl.seq_lens).to(dev)
+    dl = None if wl.decode_lens is None else torch.from_numpy(wl.decode_lens).to(dev)
+    rows = idx.Rows.decode(bt, seq, int(wl.seq_lens.max()), next_n=wl.next_n, decode_lens=dl)
+    q = torch.from_numpy(wl.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(wl.w).to(dev)
+    k = wl.topk
+    R = rows.num_rows
+    outs = torch.empty((R, k), dtype=torch.int32, device=dev)
+    ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, caches[0], rows, wl.heads, k), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        idx.idx_decode_topk(caches[i % len(caches)], rows, q, w, k, outs, ws, stream)
+
+    if args.calib:
+        # a plain elementwise copy of known size (reads and writes calib_mib
+        # MiB), for scaling the FETCH/WRITE counters
+        src = torch.ones((args.calib_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    first = outs.clone()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    assert torch.equal(first, outs), "fused decode is not deterministic across steps"
+
+    # warm-MALL reference: the same pool back to back (context only)
+    for _ in range(5):
+        idx.idx_decode_topk(caches[0], rows, q, w, k, outs, ws, stream)
+    ws_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ws_ev[0].record(stream)
+    for _ in range(20):
+        idx.idx_decode_topk(caches[0], rows, q, w, k, outs, ws, stream)
+    ws_ev[1].record(stream)
+    torch.cuda.synchronize()
+    warm_ms = ws_ev[0].elapsed_time(ws_ev[1]) / 20
+
+    keys_scored = scored_keys(wl)
+    ms_per_step = wall * 1000.0 / args.steps
+    launch_avg_ms = float(np.mean(launch_ms))
+    ab = algorithmic_bytes(wl)
+    achieved = ab["total"] / (launch_avg_ms * 1e-3) / 1e9
+    traffic, prof = load_traffic(ab["total"])
+    res = {
+        "metric": METRIC,
+        "value": keys_scored / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fp8 decode batch: 32 requests, next_n=1, seq_len ~ U[4096, 32768], page 64, "
+                               "20k-page pool, H=64, head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
+                   "name": wl.name, "requests": wl.num_req, "rows": R, "keys_scored": keys_scored,
+                   "cache_fmt": "fp8_e4m3", "pool_copies_rotated": args.copies},
+        "rows_per_s": R / (ms_per_step * 1e-3),
+        "launch_ms_avg": launch_avg_ms,
+        "launch_ms_min": float(np.min(launch_ms)),
+        "warm_mall_ms_per_step": warm_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ab["total"],
+                     "kernel": "score_kernel<128, fp8, 1, 2, fused>"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> profiles/
+# ---------------------------------------------------------------------------
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(dirs, commands):
+    """dirs: rocprofv3 output dirs of (1) --kernel-trace --stats, (2) --pmc
+    FETCH_SIZE, (3) --pmc WRITE_SIZE runs of this script."""
+    import numpy as np
+
+    from workloads import config
+
+    out = {"source_hash": kernel_source_hash(), "commands": commands}
+    stats = glob.glob(os.path.join(dirs[0], "**", "*kernel_stats.csv"), recursive=True)
+    rows = _csv_rows(stats[0])
+    lines = []
+    for r in rows:
+        if KERNEL_SUBSTR in r["Name"]:
+            out["kernel"] = r["Name"]
+            out["calls"] = int(r["Calls"])
+            out["avg_ns"] = float(r["AverageNs"])
+            out["min_ns"] = float(r["MinNs"])
+            out["max_ns"] = float(r["MaxNs"])
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+    def counter(d, cname):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        per_kernel, copy_vals = [], []
+        for r in _csv_rows(files[0]):
+            if r.get("Counter_Name") != cname:
+                continue
+            v = float(r["Counter_Value"])
+            name = r.get("Kernel_Name", "")
+            if KERNEL_SUBSTR in name:
+                per_kernel.append(v)
+            elif "copy" in name.lower() or "elementwise" in name.lower():
+                copy_vals.append(v)
+        return per_kernel, copy_vals
+
+    wl = config("C2")
+    ab = algorithmic_bytes(wl)
+    fetch, fcopy = counter(dirs[1], "FETCH_SIZE")
+    write, wcopy = counter(dirs[2], "WRITE_SIZE")
+    calib_bytes = 256 << 20
+    # counters are in KiB per dispatch; scale by what they read for a copy of known size
+    f_scale = calib_bytes / (np.median(fcopy) * 1024) if fcopy else 1.0
+    w_scale = calib_bytes / (np.median(wcopy) * 1024) if wcopy else 1.0
+    out["fetch_kib_per_launch"] = float(np.median(fetch)) if fetch else None
+    out["write_kib_per_launch"] = float(np.median(write)) if write else None
+    out["copy_fetch_kib"] = float(np.median(fcopy)) if fcopy else None
+    out["copy_write_kib"] = float(np.median(wcopy)) if wcopy else None
+    out["fetch_scale"] = f_scale
+    out["write_scale"] = w_scale
+    if fetch and write:
+        out["traffic_bytes_per_launch"] = (out["fetch_kib_per_launch"] * f_scale
+                                           + out["write_kib_per_launch"] * w_scale) * 1024
+    out["algorithmic_bytes_per_launch"] = ab["total"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", PROFILE_NAME + ".json"), "w") as f:
+        json.dump(out, f, indent=1)
+    md = [f"# Fused decode indexer, fp8 decode batch (32 x U[4096, 32768], H=64, D=128, k=2048)", "",
+          "Commands (run from the repository root on one MI355X):", ""]
+    md += [f"    {c}" for c in commands]
+    md += ["", "## rocprofv3 --kernel-trace --stats", "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"] + lines
+    md += ["", "## HBM traffic of the fused kernel (rocprofv3 --pmc, per dispatch)", "",
+           f"- FETCH_SIZE {out['fetch_kib_per_launch']} KiB, WRITE_SIZE {out['write_kib_per_launch']} KiB",
+           f"- plain 256 MiB copy reads as FETCH {out['copy_fetch_kib']} KiB / WRITE {out['copy_write_kib']} KiB "
+           f"-> scale {f_scale:.4f} / {w_scale:.4f}",
+           f"- traffic per launch {out.get('traffic_bytes_per_launch')} B vs algorithmic {ab['total']} B",
+           f"- kernel source hash {out['source_hash']}"]
+    with open(os.path.join(ROOT, "profiles", PROFILE_NAME + ".md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib", action="store_true", help="also run a plain copy for counter scaling")
+    ap.add_argument("--calib-mib", type=int, default=256)
+    ap.add_argument("--summarize-prof", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--commands", nargs="*", default=[])
+    args = ap.parse_args()
+    if args.summarize_prof:
+        summarize(args.summarize_prof, args.commands)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (multi-GPU sharding is "
+                                   "described, not implemented)"}), flush=True)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

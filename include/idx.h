@@ -27,8 +27,9 @@
  *     enqueued; on error nothing is enqueued and the status says why.
  *     Values that live in device memory (lengths, page ids) cannot be
  *     checked on the host: lengths are clamped into [0, max_seq_len], a
- *     page id outside [0, num_pages) is never dereferenced (its keys score
- *     as 0) and sets bit IDX_DEV_BAD_PAGE of the workspace status word.
+ *     page id outside [0, num_pages) is never dereferenced (page 0 is read
+ *     in its place, so the logits of those 64 positions are unspecified)
+ *     and sets bit IDX_DEV_BAD_PAGE of the workspace status word.
  *   - Nothing is thread-safe across calls that share a workspace: such calls
  *     must be ordered on one stream.
  */
@@ -146,10 +147,11 @@ int64_t idx_num_rows(const idx_rows* rows);
 
 /*
  * Bytes of device workspace `op` needs for these arguments (the caller
- * allocates it; 256-byte aligned).  The workspace must be zero-filled once
- * before its first use; every call that completes leaves its counters at
- * zero again, so a workspace can be reused (and captured in a HIP graph)
- * without clearing.  Returns 0 when the arguments are invalid.
+ * allocates it; 256-byte aligned).  Its first 256 bytes hold the device
+ * status word (see idx_read_device_status), which must be zero before the
+ * first use; nothing else needs clearing, so a workspace can be reused and
+ * calls on it captured in a HIP graph.  Calls that share a workspace must
+ * not overlap.  Returns 0 when the arguments are invalid.
  */
 size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* rows,
                            int32_t heads, int32_t k);
@@ -185,11 +187,14 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
                     int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Fused decode: scoring and top-k of every DECODE row in one launch.  Keys
- * of a request are read once for all its rows; rows with L <= k are causal
- * filled without scoring; padded rows get -1.  Output as idx_topk.
- * The workspace (idx_workspace_bytes(IDX_OP_DECODE_TOPK, ...)) holds the
- * per-row logits and the completion counters.
+ * Decode scoring and top-k of every DECODE row (the decode branch of the
+ * indexer's forward on the DeepSeek-V3.2 page: paged MQA logits, then top-k
+ * per row): two launches on `stream`, the scorer writing each row's logits
+ * into the workspace and the selector reading them.  Keys of a request are
+ * read once for all its rows; rows with L <= k are causal filled; padded
+ * rows get -1.  Output as idx_topk.  The workspace
+ * (idx_workspace_bytes(IDX_OP_DECODE_TOPK, ...)) holds the status word and
+ * the per-row logits.
  */
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
                            const float* w, int32_t heads, int32_t k, int32_t* out,

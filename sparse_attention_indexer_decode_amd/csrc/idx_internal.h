@@ -7,10 +7,13 @@ namespace idx {
 
 // Limits of this build (checked on the host before any launch).
 constexpr int kMaxHeads = 64;
-constexpr int kMaxGroups = 4096;   // row groups per scorer launch (LDS table)
+constexpr int kMaxGroups = 2048;   // row groups per scorer launch (LDS table)
 constexpr int kMaxK = 4096;        // top-k
-constexpr int kMaxReqPrefill = 1024;
-constexpr int kStatusBytes = 256;  // workspace header (status word + pad)
+constexpr int kMaxReqPrefill = 256;  // requests per prefill chunk / packed decode batch
+constexpr int kStatusBytes = 256;  // workspace header: status word + pad
+
+// Workspace header layout (int32 slots).
+constexpr int kHdrStatus = 0;
 
 struct CacheArgs {
   const uint8_t* base;

@@ -21,9 +21,7 @@ idx_status fail(idx_status st, const char* what) {
   return st;
 }
 
-constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 512;
-constexpr int kMinPagesPerBlock = 4;
 
 int row_bytes(int fmt, int d) { return fmt == IDX_FMT_FP8_E4M3 ? d + 4 : d / 2 + d / 32; }
 
@@ -92,10 +90,10 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   if (nrows > (int64_t{1} << 30)) return fail(IDX_EUNSUPPORTED, "rows: more than 2^30 rows");
   if (r->kind == IDX_ROWS_DECODE) {
     if (r->q_packed != 0 && r->q_packed != 1) return fail(IDX_EINVAL, "rows: q_packed must be 0 or 1");
-    if (r->q_packed && r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: packed queries support at most 1024 requests");
+    if (r->q_packed && r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: packed queries support at most 256 requests");
   } else {
     if (r->num_req > 0 && !r->query_start_loc) return fail(IDX_EINVAL, "rows: query_start_loc is null");
-    if (r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: a prefill chunk supports at most 1024 requests");
+    if (r->num_req > kMaxReqPrefill) return fail(IDX_EUNSUPPORTED, "rows: a prefill chunk supports at most 256 requests");
     if (r->num_req == 0 && nrows > 0) return fail(IDX_EINVAL, "rows: prefill rows without requests");
   }
   out.kind = r->kind;
@@ -129,28 +127,24 @@ int64_t scratch_stride(const RowArgs& R) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Decode-topk workspace: [status 256 B][counters][scratch logits]
-size_t counters_offset() { return kStatusBytes; }
-size_t scratch_offset(const RowArgs& R, int rg) {
-  return align_up(counters_offset() + sizeof(int32_t) * static_cast<size_t>(group_bound(R, rg)), 256);
-}
-size_t decode_ws_bytes(const RowArgs& R, int rg) {
-  return scratch_offset(R, rg) + sizeof(float) * static_cast<size_t>(R.num_rows) * scratch_stride(R);
+// Decode-topk workspace: [header 256 B][row logits, scratch_stride apart]
+size_t scratch_offset() { return kStatusBytes; }
+size_t decode_ws_bytes(const RowArgs& R) {
+  return scratch_offset() + sizeof(float) * static_cast<size_t>(R.num_rows) * scratch_stride(R);
 }
 
-template <int D, bool MX, int RG, int MT, bool F>
+template <int D, bool MX, int RG, int MT>
 hipError_t launch_score(const ScoreParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((score_kernel<D, MX, RG, MT, F>), dim3(grid), dim3(kScoreThreads), 0, s, p);
+  hipLaunchKernelGGL((score_kernel<D, MX, RG, MT>), dim3(grid), dim3(score_waves(RG, MT) * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool F>
 hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s) {
   const int d = p.cache.head_dim;
   const bool mx = p.cache.fmt == IDX_FMT_MXFP4;
   const int mt = p.heads > 32 ? 2 : 1;
 #define IDX_SCORE_CASE(D_, MX_, RG_, MT_) \
-  if (d == D_ && mx == MX_ && rg == RG_ && mt == MT_) return launch_score<D_, MX_, RG_, MT_, F>(p, grid, s);
+  if (d == D_ && mx == MX_ && rg == RG_ && mt == MT_) return launch_score<D_, MX_, RG_, MT_>(p, grid, s);
 #define IDX_SCORE_RGMT(D_, MX_) \
   IDX_SCORE_CASE(D_, MX_, 1, 1) IDX_SCORE_CASE(D_, MX_, 1, 2) IDX_SCORE_CASE(D_, MX_, 2, 1) IDX_SCORE_CASE(D_, MX_, 2, 2)
   IDX_SCORE_RGMT(128, false)
@@ -162,11 +156,13 @@ hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
+// One workgroup per CU (each wave streams a contiguous page range), fewer
+// when the launch cannot hold a page per wave.
 int score_grid(const RowArgs& R, int rg) {
   const int64_t pages = group_bound(R, rg) * ceil_div(R.max_len, kPage);
-  int64_t g = ceil_div(pages, kMinPagesPerBlock);
-  const int64_t gmax = static_cast<int64_t>(device_cu_count()) * 2;
-  if (g > gmax) g = gmax;
+  int64_t g = device_cu_count();
+  const int64_t need = ceil_div(pages, 8);
+  if (g > need) g = need;
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
@@ -178,6 +174,17 @@ idx_status check_queries(const uint16_t* q, const float* w, int heads) {
   if ((reinterpret_cast<uintptr_t>(q) & 15) != 0) return fail(IDX_EINVAL, "q must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(w) & 3) != 0) return fail(IDX_EINVAL, "w must be 4-byte aligned");
   return IDX_OK;
+}
+
+idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, int k, int32_t* out, hipStream_t s) {
+  TopkParams p{};
+  p.logits = logits;
+  p.stride = stride;
+  p.rows = R;
+  p.k = k;
+  p.out = out;
+  hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0, s, p);
+  return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
 }
 
 idx_status check_ws(void* ws, size_t have, size_t need) {
@@ -209,7 +216,7 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
   if (op == IDX_OP_LOGITS) return kStatusBytes;
   if (op == IDX_OP_DECODE_TOPK) {
     if (R.kind != IDX_ROWS_DECODE || k < 1 || k > kMaxK) return 0;
-    return decode_ws_bytes(R, pick_rg(R));
+    return decode_ws_bytes(R);
   }
   return 0;
 }
@@ -227,7 +234,7 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
   if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
   if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
   const int rg = pick_rg(R);
-  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 4096)");
+  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
   if (R.num_rows == 0 || R.max_len == 0) return IDX_OK;
   ScoreParams p{};
   p.cache = C;
@@ -235,12 +242,11 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
   p.q = q;
   p.w = w;
   p.heads = heads;
-  p.k = 0;
   p.logits = logits;
   p.logits_stride = logits_stride;
-  p.status = static_cast<uint32_t*>(workspace);
+  p.header = static_cast<int32_t*>(workspace);
   p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-  const hipError_t e = dispatch_score<false>(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
+  const hipError_t e = dispatch_score(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
 }
 
@@ -255,15 +261,7 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
   if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
   if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
-  TopkParams p{};
-  p.logits = logits;
-  p.stride = logits_stride;
-  p.rows = R;
-  p.k = k;
-  p.out = out;
-  hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
-  return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+  return launch_topk(logits, logits_stride, R, k, out, static_cast<hipStream_t>(stream));
 }
 
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
@@ -280,25 +278,28 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
   if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
   if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
   const int rg = pick_rg(R);
-  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 4096)");
-  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R, rg))) != IDX_OK) return st;
+  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
+  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R))) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
+  // scorer into the workspace's row logits, then top-k of each row (the
+  // kernel boundary orders the two)
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  ScoreParams p{};
-  p.cache = C;
-  p.rows = R;
-  p.q = q;
-  p.w = w;
-  p.heads = heads;
-  p.k = k;
-  p.logits = reinterpret_cast<float*>(ws + scratch_offset(R, rg));
-  p.logits_stride = scratch_stride(R);
-  p.out = out;
-  p.counters = reinterpret_cast<int32_t*>(ws + counters_offset());
-  p.status = reinterpret_cast<uint32_t*>(ws);
-  p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-  const hipError_t e = dispatch_score<true>(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+  float* logits = reinterpret_cast<float*>(ws + scratch_offset());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (R.max_len > 0) {
+    ScoreParams p{};
+    p.cache = C;
+    p.rows = R;
+    p.q = q;
+    p.w = w;
+    p.heads = heads;
+    p.logits = logits;
+    p.logits_stride = scratch_stride(R);
+    p.header = reinterpret_cast<int32_t*>(ws);
+    p.num_groups = static_cast<int32_t>(group_bound(R, rg));
+    if (dispatch_score(p, rg, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
+  }
+  return launch_topk(logits, scratch_stride(R), R, k, out, s);
 }
 
 idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream) {

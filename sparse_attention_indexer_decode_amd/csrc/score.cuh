@@ -3,16 +3,23 @@
 //
 // Work decomposition.  Rows are bundled into "groups" of up to RG rows that
 // share one request (the next_n decode rows of a request, or consecutive
-// query rows of a prefill request); a group reads the pages of its request
-// once for all its rows.  The pages of all groups form one global list
-// (prefix sums in LDS, rebuilt by every workgroup from the device lengths, so
-// the host never reads device data); each workgroup takes a contiguous slice
-// of that list and its four waves take every fourth page of the slice.
+// query rows of a prefill request); a group reads its request's pages once
+// for all its rows.  Every workgroup (one per CU, eight waves) builds the
+// prefix of pages over groups in LDS from the device lengths (the host never
+// reads them); the global page list is then cut into equal contiguous ranges,
+// one per wave.
 //
-// Per page (64 keys) a wave: copies the page's token rows into its LDS
-// buffer with 16-byte loads (issued one page ahead into registers), decodes
-// its B fragments (32 keys per 32x32x16 MFMA) from LDS to bf16, and runs
-// bf16 MFMAs against query fragments held in registers for the whole group.
+// Memory pipeline.  Each wave streams its pages through a two-page ring in
+// LDS filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KiB per
+// instruction): while page j is scored from one buffer, page j+1 is already
+// in flight into the other, and page j+2 is requested as soon as page j's
+// buffer is consumed.  No staging registers are used, and the waits are
+// explicit vmcnt counts (loads retire in order; every wait leaves exactly the
+// loads issued after the page it needs outstanding).
+//
+// Per page (64 keys) a wave decodes its B fragments (32 keys per 32x32x16
+// MFMA) from LDS to bf16 and runs bf16 MFMAs against query fragments held in
+// registers.
 //
 // Precision.  Every e4m3 code and every e2m1 value times its power-of-two
 // MX block scale is exactly a bf16, and q is bf16, so the products are
@@ -29,12 +36,17 @@
 // same dims, so the contraction covers all D.  Accumulator lane l, register
 // v: key l % 32, head 8 (v / 4) + 4 (l / 32) + v % 4, so the head sum is 16
 // in-lane terms per M-tile plus one swap of the lane halves.
+//
 #pragma once
 
 #include "device_common.cuh"
-#include "select.cuh"
 
 namespace idx {
+
+// Waves per workgroup (one workgroup per CU): eight, or four when a wave
+// holds the query fragments of two rows of 64 heads (the register file of a
+// SIMD then holds one such wave).
+constexpr int score_waves(int rg, int mt) { return rg * mt >= 4 ? 4 : 8; }
 
 struct ScoreParams {
   CacheArgs cache;
@@ -42,89 +54,90 @@ struct ScoreParams {
   const uint16_t* q;
   const float* w;
   int32_t heads;
-  int32_t k;              // fused mode: top-k
   float* logits;          // row r at logits + r * logits_stride (+ column base)
   int64_t logits_stride;
-  int32_t* out;           // fused mode: [rows, k]
-  int32_t* counters;      // fused mode: per-group completion counters
-  uint32_t* status;
-  int32_t num_groups;     // host bound on groups (table size)
+  int32_t* header;        // workspace header: status word
+  int32_t num_groups;     // decode: groups (prefill: derived on the device)
 };
 
 template <int D, bool MX>
 struct Geometry {
   static constexpr int kRowBytes = MX ? (D / 2 + D / 32) : (D + 4);
   static constexpr int kPageBytes = kPage * kRowBytes;
-  static constexpr int kChunks = (kPageBytes / 16 + kWave - 1) / kWave;  // 16-B loads per lane
-  static constexpr int kKSteps = D / 16;  // 32x32x16 steps over the head dim
+  // A page moves to LDS as kWide 1 KiB loads (16 B per lane) plus kNarrow
+  // 256 B loads (4 B per lane), exactly its bytes.
+  static constexpr int kWide = kPageBytes / 1024;
+  static constexpr int kNarrow = (kPageBytes % 1024) / 256;
+  static constexpr int kLoads = kWide + kNarrow;
+  static constexpr int kKSteps = D / 16;  // 32x32x16 steps
+  static_assert(kPageBytes % 256 == 0, "page must split into 256-byte loads");
+  static_assert(kLoads <= 15, "loads per page must fit a vmcnt immediate");
 };
 
-template <int D, bool MX, int RG>
+template <int D, bool MX, int RG, int NWV>
 struct ScoreShared {
-  int gprefix[kMaxGroups + 1];
+  int page_prefix[kMaxGroups + 1];     // pages before each group
   int req_tab[4][kMaxReqPrefill + 1];  // prefill: groups, rows, columns, first query; decode: packed offsets
-  float wbuf[4][RG][kMaxHeads];
-  int misc[8];
-  union {
-    uint8_t page[4][Geometry<D, MX>::kPageBytes];
-    SelectShared<256> sel;
-  } u;
+  float wbuf[NWV][RG][kMaxHeads];
+  int misc[16];
+  uint8_t page[NWV][2][Geometry<D, MX>::kPageBytes];
 };
 
 struct GroupDesc {
-  int b;         // request
-  int nrows;     // rows in the group
-  int row0;      // output row of the first row (grid row or chunk row)
-  int row_step;  // output row stride between the group's rows (1)
-  int col0;      // logits column base (prefill ks)
+  int b;      // request
+  int nrows;  // rows in the group
+  int row0;   // output row of the first row (grid row or chunk row)
+  int col0;   // logits column base (prefill ks)
   int Lmax;
 };
-
-// ---------------------------------------------------------------------------
-// Group tables (built by every workgroup in LDS)
-// ---------------------------------------------------------------------------
 
 template <int RG>
 __device__ __forceinline__ int groups_per_request(int next_n) {
   return (next_n + RG - 1) / RG;
 }
 
-// Rows of group g and their lengths.  L[rho] = 0 marks an empty row slot.
+// Request of group g (decode: arithmetic; prefill: search of the LDS table).
 template <int RG>
-__device__ __forceinline__ GroupDesc describe_group(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1],
-                                                    int g, int (&L)[RG], int (&qrow)[RG]) {
+__device__ __forceinline__ int group_request(const RowArgs& R, const int (*req_tab)[kMaxReqPrefill + 1], int g) {
+  if (R.kind == 0) return g / groups_per_request<RG>(R.next_n);
+  int lo = 0, hi = R.num_req;  // last b with groups_before[b] <= g
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (req_tab[0][mid] <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rows of group g: their key counts L (0 = empty slot), the q/w row each
+// reads (qload, -1 = none) and whether the row is real (w is zeroed for
+// padded decode slots, whose q row exists but must not count).
+template <int RG>
+__device__ __forceinline__ GroupDesc describe_group(const RowArgs& R, const int (*req_tab)[kMaxReqPrefill + 1],
+                                                    int g, int b, int (&L)[RG], int (&qload)[RG],
+                                                    bool (&real)[RG]) {
   GroupDesc d;
-  const RowArgs& R = p.rows;
+  d.b = b;
+  d.Lmax = 0;
+  d.nrows = 0;
   if (R.kind == 0) {
-    const int gpr = groups_per_request<RG>(R.next_n);
-    const int b = g / gpr;
-    const int j = g - b * gpr;
+    const int j = g - b * groups_per_request<RG>(R.next_n);
     int seq = R.seq_lens[b];
     seq = seq > R.max_len ? R.max_len : seq;
     const int dl = R.decode_lens ? R.decode_lens[b] : R.next_n;
-    d.b = b;
     d.row0 = b * R.next_n + j * RG;
-    d.row_step = 1;
     d.col0 = 0;
-    d.nrows = 0;
-    d.Lmax = 0;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int i = j * RG + r;
       const bool exists = i < R.next_n;
+      real[r] = exists && i < dl;
       L[r] = exists ? decode_row_len(seq, dl, i, R.max_len) : 0;
-      qrow[r] = (exists && i < dl) ? (R.q_packed ? req_tab[0][b] + i : b * R.next_n + i) : -1;
+      if (R.q_packed) qload[r] = real[r] ? req_tab[0][b] + i : -1;
+      else qload[r] = exists ? b * R.next_n + i : -1;
       d.nrows += exists ? 1 : 0;
       d.Lmax = L[r] > d.Lmax ? L[r] : d.Lmax;
     }
   } else {
-    // binary search: last b with groups_before[b] <= g
-    int lo = 0, hi = R.num_req;  // invariant tab[lo] <= g < tab[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (req_tab[0][mid] <= g) lo = mid; else hi = mid;
-    }
-    const int b = lo;
     const int gi = g - req_tab[0][b];
     const int rows_b = req_tab[1][b + 1] - req_tab[1][b];
     const int first_row = req_tab[1][b] + gi * RG;
@@ -132,109 +145,83 @@ __device__ __forceinline__ GroupDesc describe_group(const ScoreParams& p, const 
     int seq = R.seq_lens[b];
     seq = seq > R.max_len ? R.max_len : seq;
     const int qlen = R.qsl[b + 1] - R.qsl[b];
-    d.b = b;
     d.row0 = first_row;
-    d.row_step = 1;
     d.col0 = req_tab[2][b];
     d.nrows = rows_b - gi * RG < RG ? rows_b - gi * RG : RG;
-    d.Lmax = 0;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const bool exists = r < d.nrows;
       int Lr = seq - qlen + j0 + r + 1;
       Lr = Lr < 0 ? 0 : (Lr > seq ? seq : Lr);
       L[r] = exists ? Lr : 0;
-      qrow[r] = exists ? first_row + r : -1;
+      real[r] = exists;
+      qload[r] = exists ? first_row + r : -1;
       d.Lmax = L[r] > d.Lmax ? L[r] : d.Lmax;
     }
   }
   return d;
 }
 
-// Fills sm.gprefix[0..NG] (page prefix over groups) and the request tables;
-// returns NG.  Called by all 256 threads.
-template <int RG, bool kFused, class SM>
-__device__ int build_group_tables(const ScoreParams& p, SM& sm) {
-  const RowArgs& R = p.rows;
+// Request tables in LDS: packed decode offsets, or (prefill) per request the
+// groups/rows/columns before it and its first query index in the slice.
+// Returns the number of groups (decode: num_req * groups per request).
+template <int RG, int NT, class SM>
+__device__ int build_request_tables(const RowArgs& R, SM& sm) {
   const int tid = threadIdx.x;
-  int NG;
   if (R.kind == 0) {
-    NG = R.num_req * groups_per_request<RG>(R.next_n);
     if (R.q_packed) {
-      // exclusive prefix of decode_lens -> packed token offsets
       int run = 0;
-      for (int base = 0; base < R.num_req; base += 256) {
+      for (int base = 0; base < R.num_req; base += NT) {
         const int b = base + tid;
         const int v = (b < R.num_req) ? (R.decode_lens ? R.decode_lens[b] : R.next_n) : 0;
         int tot;
-        const int ex = block_exclusive_scan<256>(v, tot, sm.misc);
+        const int ex = block_exclusive_scan<NT>(v, tot, sm.misc);
         if (b < R.num_req) sm.req_tab[0][b] = run + ex;
         run += tot;
       }
       __syncthreads();
     }
-  } else {
-    // per request: rows of the chunk slice, groups, column base, first query index
-    const int q0 = R.qsl[0];
-    int run_g = 0, run_r = 0, run_c = 0;
-    for (int base = 0; base < R.num_req; base += 256) {
-      const int b = base + tid;
-      int rows_b = 0, cols_b = 0, first_j = 0;
-      if (b < R.num_req) {
-        const int s = R.qsl[b] - q0, e = R.qsl[b + 1] - q0;
-        const int lo = s > R.q_begin ? s : R.q_begin;
-        const int hi = e < R.q_end ? e : R.q_end;
-        rows_b = hi > lo ? hi - lo : 0;
-        first_j = lo - s;
-        int seq = R.seq_lens[b];
-        cols_b = seq > R.max_len ? R.max_len : (seq < 0 ? 0 : seq);
-      }
-      const int gr = (rows_b + RG - 1) / RG;
-      int tg, tr, tc;
-      const int eg = block_exclusive_scan<256>(gr, tg, sm.misc);
-      const int er = block_exclusive_scan<256>(rows_b, tr, sm.misc);
-      const int ec = block_exclusive_scan<256>(cols_b, tc, sm.misc);
-      if (b < R.num_req) {
-        sm.req_tab[0][b] = run_g + eg;
-        sm.req_tab[1][b] = run_r + er;
-        sm.req_tab[2][b] = run_c + ec;
-        sm.req_tab[3][b] = first_j;
-      }
-      run_g += tg;
-      run_r += tr;
-      run_c += tc;
-    }
-    if (tid == 0) {
-      sm.req_tab[0][R.num_req] = run_g;
-      sm.req_tab[1][R.num_req] = run_r;
-      sm.req_tab[2][R.num_req] = run_c;
-    }
-    __syncthreads();
-    NG = run_g;
+    return R.num_req * groups_per_request<RG>(R.next_n);
   }
-  // page prefix over groups
-  int run = 0;
-  for (int base = 0; base < NG; base += 256) {
-    const int g = base + tid;
-    int np = 0;
-    if (g < NG) {
-      int L[RG], qr[RG];
-      GroupDesc d = describe_group<RG>(p, sm.req_tab, g, L, qr);
-      np = (d.Lmax + kPage - 1) / kPage;
-      if (kFused && d.Lmax <= p.k) np = 0;  // causal fill only, nothing to score
+  const int q0 = R.qsl[0];
+  int run_g = 0, run_r = 0, run_c = 0;
+  for (int base = 0; base < R.num_req; base += NT) {
+    const int b = base + tid;
+    int rows_b = 0, cols_b = 0, first_j = 0;
+    if (b < R.num_req) {
+      const int s = R.qsl[b] - q0, e = R.qsl[b + 1] - q0;
+      const int lo = s > R.q_begin ? s : R.q_begin;
+      const int hi = e < R.q_end ? e : R.q_end;
+      rows_b = hi > lo ? hi - lo : 0;
+      first_j = lo - s;
+      const int seq = R.seq_lens[b];
+      cols_b = seq > R.max_len ? R.max_len : (seq < 0 ? 0 : seq);
     }
-    int tot;
-    const int ex = block_exclusive_scan<256>(np, tot, sm.misc);
-    if (g < NG) sm.gprefix[g] = run + ex;
-    run += tot;
+    int tg, tr, tc;
+    const int eg = block_exclusive_scan<NT>((rows_b + RG - 1) / RG, tg, sm.misc);
+    const int er = block_exclusive_scan<NT>(rows_b, tr, sm.misc);
+    const int ec = block_exclusive_scan<NT>(cols_b, tc, sm.misc);
+    if (b < R.num_req) {
+      sm.req_tab[0][b] = run_g + eg;
+      sm.req_tab[1][b] = run_r + er;
+      sm.req_tab[2][b] = run_c + ec;
+      sm.req_tab[3][b] = first_j;
+    }
+    run_g += tg;
+    run_r += tr;
+    run_c += tc;
   }
-  if (tid == 0) sm.gprefix[NG] = run;
+  if (tid == 0) {
+    sm.req_tab[0][R.num_req] = run_g;
+    sm.req_tab[1][R.num_req] = run_r;
+    sm.req_tab[2][R.num_req] = run_c;
+  }
   __syncthreads();
-  return NG;
+  return run_g;
 }
 
 // ---------------------------------------------------------------------------
-// Query fragments (a wave loads the A operands of one group)
+// Operand fragments
 // ---------------------------------------------------------------------------
 
 template <int D, int RG, int MT>
@@ -242,9 +229,12 @@ struct QFrag {
   v8bf a[RG][MT][D / 16];
 };
 
+// A fragments of the group's rows (this lane: head 32 mt + lane % 32, dims
+// [g D/2, g D/2 + D/2)).  Rows or heads that do not exist read row 0 / head 0
+// instead (loads stay unconditional); their head weights are zero, so they
+// add nothing.
 template <int D, int RG, int MT>
-__device__ __forceinline__ void prepare_query(const ScoreParams& p, const int (&qrow)[RG],
-                                              QFrag<D, RG, MT>& f, float (*wbuf)[kMaxHeads]) {
+__device__ __forceinline__ void load_query(const ScoreParams& p, const int (&qload)[RG], QFrag<D, RG, MT>& f) {
   const int lane = lane_id();
   const int m = lane & 31;
   const int g = lane >> 5;
@@ -253,18 +243,22 @@ __device__ __forceinline__ void prepare_query(const ScoreParams& p, const int (&
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int h = 32 * mt + m;
-      const bool valid = qrow[r] >= 0 && h < p.heads;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          p.q + (static_cast<int64_t>(valid ? qrow[r] : 0) * p.heads + (valid ? h : 0)) * D + g * (D / 2));
+      const bool valid = qload[r] >= 0 && h < p.heads;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          p.q + (static_cast<int64_t>(valid ? qload[r] : 0) * p.heads + (valid ? h : 0)) * D + g * (D / 2));
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const uint4 v = valid ? src[s] : make_uint4(0, 0, 0, 0);
-        f.a[r][mt][s] = __builtin_bit_cast(v8bf, v);
-      }
-      if (g == 0) wbuf[r][h] = valid ? p.w[static_cast<int64_t>(qrow[r]) * p.heads + h] : 0.0f;
+      for (int s = 0; s < D / 16; ++s) f.a[r][mt][s] = __builtin_bit_cast(v8bf, src[s]);
     }
-    if (MT == 1 && lane < 32) wbuf[r][32 + lane] = 0.0f;
   }
+}
+
+// max(x, 0) in one instruction: as signed integers, negative floats
+// (including -0.0) are below 0 and non-negative floats keep their order, so
+// an integer max with 0 is the float ReLU (fmaxf would add a canonicalizing
+// max in front of the MFMA result).
+__device__ __forceinline__ float relu(float x) {
+  const int i = __float_as_int(x);
+  return __int_as_float(i > 0 ? i : 0);
 }
 
 // 2^(e - 127) as an fp32 (e = 0 is the subnormal 2^-127, e = 255 is NaN).
@@ -284,22 +278,143 @@ __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (
     for (int s = 0; s < D / 16; ++s) {
       const uint32_t x = w32[s];
       const float f = sc[s / 4];
-      const v2bf e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 0);
-      const v2bf e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 1);
-      const v2bf e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 2);
-      const v2bf e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 3);
-      b[s] = v8bf{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+      const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 0)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 1)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 2)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 3))};
+      b[s] = __builtin_bit_cast(v8bf, r);
     }
   } else {
     const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rowp + g * (D / 2));
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const uint32_t x0 = w32[2 * s], x1 = w32[2 * s + 1];
-      const v2bf e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
-      const v2bf e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
-      const v2bf e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
-      const v2bf e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
-      b[s] = v8bf{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+      const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true))};
+      b[s] = __builtin_bit_cast(v8bf, r);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS page loads
+// ---------------------------------------------------------------------------
+
+// One direct global -> LDS load: lane i's `size` bytes at gptr land at LDS
+// byte address lds + size * i.  Written as inline assembly so that the
+// compiler's own wait-count tracking, which cannot tell the two ring buffers
+// apart and would wait for every request before any LDS read, stays out of
+// it; the waits below count these loads instead.  (An asm load also makes any
+// wait the compiler computes for its own loads stricter, never weaker.)
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p)));
+}
+
+// Requests page `phys` into the LDS buffer at byte address `lds`: byte i of
+// the page lands at lds + i.  Always issues exactly kLoads loads.
+template <int D, bool MX>
+__device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_t lds) {
+  using Geo = Geometry<D, MX>;
+  const int lane = lane_id();
+  const uint8_t* src = p.cache.base + static_cast<int64_t>(phys) * p.cache.page_bytes;
+#pragma unroll
+  for (int c = 0; c < Geo::kWide; ++c) lds_dma16(src + 1024 * c + 16 * lane, lds + 1024 * c);
+#pragma unroll
+  for (int c = 0; c < Geo::kNarrow; ++c)
+    lds_dma4(src + 1024 * Geo::kWide + 256 * c + 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
+}
+
+// s_waitcnt for vector memory only (vmcnt <= n; the gfx9 encoding keeps
+// vmcnt in bits [3:0] and [15:14] and leaves expcnt and lgkmcnt at their
+// maxima).  The builtin keeps the compiler's wait-count model in step (it
+// learns that its own older loads are complete); the empty asm keeps LDS
+// reads of the DMA'd data from moving above the wait.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_all_loads() { wait_vmcnt<0>(); }
+
+// Waits until at most kLoads vector-memory operations are outstanding: every
+// page requested before the most recent one has landed in LDS (vector memory
+// operations complete in issue order).
+template <int D, bool MX>
+__device__ __forceinline__ void wait_all_but_last_page() {
+  wait_vmcnt<Geometry<D, MX>::kLoads>();
+}
+
+// Head weights of the group's rows as the accumulator layout needs them:
+// lane half g, M-tile mt, register v -> head 32 mt + 8 (v / 4) + 4 g + v % 4.
+template <int RG, int MT>
+struct WFrag {
+  float v[RG][MT][16];
+};
+
+// Output of one row: a raw buffer over its L logits, so that stores of keys
+// at or past L (and of the lane half that does not store) fall outside the
+// buffer and are dropped by the hardware, with no branch around the store.
+typedef __amdgpu_buffer_rsrc_t RowOut;
+
+__device__ __forceinline__ RowOut row_out(float* base, int L) {
+  // the descriptor lives in scalar registers: make its (wave-uniform)
+  // fields visibly uniform
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(L > 0 ? L * 4 : 0);
+  float* u = reinterpret_cast<float*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, n, 0x00020000);
+}
+
+// Scores the 64 keys of the page in LDS for every row of the group and
+// stores logit t = 64 pg + key of each.
+template <int D, bool MX, int RG, int MT>
+__device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, MT>& wf, const QFrag<D, RG, MT>& qf,
+                                           const RowOut (&out)[RG], int pg) {
+  using Geo = Geometry<D, MX>;
+  constexpr int KS = Geo::kKSteps;
+  constexpr int RB = Geo::kRowBytes;
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int g = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int key = nt * 32 + n;
+    const uint8_t* rowp = buf + key * RB;
+    v8bf bfr[KS];
+    key_fragments<D, MX>(rowp, g, bfr);
+    const float key_scale = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
+    const int off = g == 0 ? (pg * kPage + key) * 4 : 0x7FFFFFF0;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      float partial = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        v16f acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) partial += wf.v[r][mt][v] * relu(acc[v]);
+      }
+      // add the other lane half's heads (v_permlane32_swap: both halves end
+      // up holding lo + hi)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(partial), __float_as_uint(partial), false, false);
+      const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * key_scale;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out[r], off, 0, 0);
     }
   }
 }
@@ -308,205 +423,154 @@ __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (
 // The scorer kernel
 // ---------------------------------------------------------------------------
 
-template <int D, bool MX, int RG, int MT, bool kFused>
-__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-  using Geo = Geometry<D, MX>;
-  constexpr int KS = Geo::kKSteps;
-  constexpr int RB = Geo::kRowBytes;
-  __shared__ ScoreShared<D, MX, RG> sm;
+// Page j of the global list -> (group, page within group) by walking the
+// prefix from the previous group (pages of a wave are visited in order).
+__device__ __forceinline__ int advance_group(const int* page_prefix, int g, int pgl) {
+  while (pgl >= page_prefix[g + 1]) ++g;
+  return g;
+}
 
+// Group holding global page j: the last group whose first page is <= j
+// (groups without pages share their first page with the next group).
+__device__ __forceinline__ int group_of_page(const int* page_prefix, int ng, int j) {
+  int lo = 0, hi = ng;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (page_prefix[mid] <= j) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Physical ids of global pages jb + lane (one per lane, page 0 past j1).  Ids
+// outside the pool set the status flag and read page 0 instead.
+template <int RG>
+__device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_prefix,
+                                        const int (*req_tab)[kMaxReqPrefill + 1], int ng, int jb, int j1) {
+  const int j = jb + lane_id();
+  if (j >= j1) return 0;
+  const RowArgs& R = p.rows;
+  const int g = group_of_page(page_prefix, ng, j);
+  const int b = group_request<RG>(R, req_tab, g);
+  const int id = R.block_table[static_cast<int64_t>(b) * R.bt_stride + (j - page_prefix[g])];
+  const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
+  if (!ok) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, 1u);
+  return ok ? id : 0;
+}
+
+template <int D, bool MX, int RG, int MT>
+__global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(ScoreParams p) {
+  constexpr int kScoreWaves = score_waves(RG, MT);
+  constexpr int kScoreThreads = kScoreWaves * kWave;
+  __shared__ ScoreShared<D, MX, RG, kScoreWaves> sm;
+  const RowArgs& R = p.rows;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = lane & 31;
-  const int g = lane >> 5;
+  const bool tables = R.kind != 0 || R.q_packed;
+  const int NG = tables ? build_request_tables<RG, kScoreThreads>(R, sm) : p.num_groups;
 
-  const int NG = build_group_tables<RG, kFused>(p, sm);
-  const int P = sm.gprefix[NG];
-
-  // Fused: rows of groups that need no scoring are written here.
-  if (kFused) {
-    for (int gg = blockIdx.x; gg < NG; gg += gridDim.x) {
-      if (sm.gprefix[gg + 1] != sm.gprefix[gg]) continue;
-      int L[RG], qr[RG];
-      GroupDesc d = describe_group<RG>(p, sm.req_tab, gg, L, qr);
-      for (int r = 0; r < d.nrows; ++r) {
-        int32_t* o = p.out + static_cast<int64_t>(d.row0 + r) * p.k;
-        for (int j = tid; j < p.k; j += 256) o[j] = (j < L[r]) ? j : -1;
-      }
-    }
-  }
-
-  const int64_t G = gridDim.x;
-  const int r0 = static_cast<int>((static_cast<int64_t>(P) * blockIdx.x) / G);
-  const int r1 = static_cast<int>((static_cast<int64_t>(P) * (blockIdx.x + 1)) / G);
-
-  uint8_t* buf = sm.u.page[wave];
-  float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
-
-  QFrag<D, RG, MT> qf;
-  int L[RG], qrow[RG];
-  GroupDesc gd;
-  gd.b = -1;
-  int cur_g = -1;
-
-  // group containing page r0 + wave: last gi with gprefix[gi] <= page
-  // (groups without pages share their prefix with the next group; the walk
-  // below steps over them)
-  int gi = 0;
-  if (r0 + wave < r1) {
-    int lo = 0, hi = NG;
-    const int target = r0 + wave;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.gprefix[mid] <= target) lo = mid; else hi = mid;
-    }
-    gi = lo;
-  }
-
-  uint4 stage[Geo::kChunks];
-
-  // physical page of global page index `pgl` in group `grp` (descriptor d)
-  auto issue_load = [&](int pgl, const GroupDesc& d, int grp) {
-    const int pg = pgl - sm.gprefix[grp];
-    const int phys = p.rows.block_table[static_cast<int64_t>(d.b) * p.rows.bt_stride + pg];
-    const bool ok = phys >= 0 && static_cast<int64_t>(phys) < p.cache.num_pages;
-    if (!ok && lane == 0) atomicOr(p.status, 1u);
-    const uint4* src = reinterpret_cast<const uint4*>(p.cache.base + static_cast<int64_t>(ok ? phys : 0) * p.cache.page_bytes);
-#pragma unroll
-    for (int c = 0; c < Geo::kChunks; ++c) {
-      const int idx16 = c * kWave + lane;
-      stage[c] = (ok && idx16 < Geo::kPageBytes / 16) ? src[idx16] : make_uint4(0, 0, 0, 0);
-    }
-  };
-
-  int pg_cur = r0 + wave;
-  GroupDesc nd;
-  int nd_g = -1;
-  int ndL[RG], ndq[RG];
-  if (pg_cur < r1) {
-    while (pg_cur >= sm.gprefix[gi + 1]) ++gi;
-    nd = describe_group<RG>(p, sm.req_tab, gi, ndL, ndq);
-    nd_g = gi;
-    issue_load(pg_cur, nd, gi);
-  }
-
-  for (; pg_cur < r1; pg_cur += 4) {
-    // the group of the current page is (nd, nd_g)
-    if (nd_g != cur_g) {
-      cur_g = nd_g;
-      gd = nd;
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        L[r] = ndL[r];
-        qrow[r] = ndq[r];
-      }
-      prepare_query<D, RG, MT>(p, qrow, qf, wbuf);
-    }
-    const int pg_in_group = pg_cur - sm.gprefix[cur_g];
-
-    // stage -> LDS
-#pragma unroll
-    for (int c = 0; c < Geo::kChunks; ++c) {
-      const int idx16 = c * kWave + lane;
-      if (idx16 < Geo::kPageBytes / 16) reinterpret_cast<uint4*>(buf)[idx16] = stage[c];
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // prefetch the next page of this wave
-    const int pg_next = pg_cur + 4;
-    if (pg_next < r1) {
-      while (pg_next >= sm.gprefix[gi + 1]) ++gi;
-      if (gi != nd_g) {
-        nd = describe_group<RG>(p, sm.req_tab, gi, ndL, ndq);
-        nd_g = gi;
-      }
-      issue_load(pg_next, nd, gi);
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int key = nt * 32 + n;
-      const uint8_t* rowp = buf + key * RB;
-      v8bf bfr[KS];
-      key_fragments<D, MX>(rowp, g, bfr);
-      float key_scale = 1.0f;
-      if (!MX) key_scale = *reinterpret_cast<const float*>(rowp + D);
-
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        float partial = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v16f acc = {};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc, 0, 0, 0);
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 wv = *reinterpret_cast<const float4*>(&wbuf[r][32 * mt + 8 * i4 + 4 * g]);
-            partial += wv.x * fmaxf(acc[4 * i4 + 0], 0.0f);
-            partial += wv.y * fmaxf(acc[4 * i4 + 1], 0.0f);
-            partial += wv.z * fmaxf(acc[4 * i4 + 2], 0.0f);
-            partial += wv.w * fmaxf(acc[4 * i4 + 3], 0.0f);
-          }
-        }
-        const float total = (partial + __shfl_xor(partial, 32, kWave)) * key_scale;
-        const int t = pg_in_group * kPage + key;
-        if (g == 0 && r < gd.nrows && t < L[r]) {
-          const int64_t row = gd.row0 + r;
-          p.logits[row * p.logits_stride + gd.col0 + t] = total;
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  if (!kFused) return;
-
-  // ---- fused top-k: the workgroup that completes a group selects its rows
-  __threadfence();
-  __syncthreads();
-  if (r0 >= r1) return;
-  int glo, ghi;
+  // pages per group -> prefix in LDS
   {
-    int lo = 0, hi = NG;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.gprefix[mid] <= r0) lo = mid; else hi = mid;
+    int run = 0;
+    for (int base = 0; base < NG; base += kScoreThreads) {
+      const int g = base + tid;
+      int np = 0;
+      if (g < NG) {
+        int L[RG], ql[RG];
+        bool rl[RG];
+        const GroupDesc d = describe_group<RG>(R, sm.req_tab, g, group_request<RG>(R, sm.req_tab, g), L, ql, rl);
+        np = (d.Lmax + kPage - 1) / kPage;
+      }
+      int tot;
+      const int ex = block_exclusive_scan<kScoreThreads>(np, tot, sm.misc);
+      if (g < NG) sm.page_prefix[g] = run + ex;
+      run += tot;
     }
-    glo = lo;
-    lo = 0;
-    hi = NG;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.gprefix[mid] <= r1 - 1) lo = mid; else hi = mid;
-    }
-    ghi = lo;
-  }
-  for (int gg = glo; gg <= ghi; ++gg) {
-    const int a0 = sm.gprefix[gg], a1 = sm.gprefix[gg + 1];
-    if (a1 == a0) continue;
-    const int c = (r1 < a1 ? r1 : a1) - (r0 > a0 ? r0 : a0);
-    if (c <= 0) continue;
-    if (tid == 0) {
-      const int old = atomicAdd(&p.counters[gg], c);
-      const int last = (old + c == a1 - a0) ? 1 : 0;
-      if (last) p.counters[gg] = 0;
-      sm.misc[0] = last;
-    }
+    if (tid == 0) sm.page_prefix[NG] = run;
     __syncthreads();
-    const int last = sm.misc[0];
-    __syncthreads();
-    if (!last) continue;
-    __threadfence();
-    int Lg[RG], qg[RG];
-    GroupDesc d = describe_group<RG>(p, sm.req_tab, gg, Lg, qg);
-    for (int r = 0; r < d.nrows; ++r) {
-      const int64_t row = d.row0 + r;
-      select_row<256>(p.logits + row * p.logits_stride, Lg[r], p.k, p.out + row * p.k, sm.u.sel);
-      __syncthreads();
+  }
+  const int P = sm.page_prefix[NG];
+
+  // this wave's contiguous page range
+  const int64_t NW = static_cast<int64_t>(gridDim.x) * kScoreWaves;
+  const int64_t W = static_cast<int64_t>(blockIdx.x) * kScoreWaves + __builtin_amdgcn_readfirstlane(wave);
+  const int j0 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * W / NW));
+  const int j1 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * (W + 1) / NW));
+
+  float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
+  const uint32_t buf_lds[2] = {lds_addr(sm.page[wave][0]), lds_addr(sm.page[wave][1])};
+
+  if (j0 < j1) {
+    // Page ids come in batches of 64 (lane i: page jb + i), so that no
+    // compiler-visible load sits between page requests; each batch costs one
+    // drain of the requests in flight.
+    int jb = j0;
+    int ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+    auto id_of = [&](int j) -> int {  // j < j1
+      if (j - jb >= kWave) {
+        jb = j;
+        ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+      }
+      return __builtin_amdgcn_readlane(ids, j - jb);
+    };
+    const int id0 = id_of(j0);
+    const int id1 = j0 + 1 < j1 ? id_of(j0 + 1) : 0;
+    wait_all_loads();  // nothing the compiler loaded before is still in flight
+    dma_page<D, MX>(p, id0, buf_lds[0]);
+    if (j0 + 1 < j1) dma_page<D, MX>(p, id1, buf_lds[1]);
+
+    QFrag<D, RG, MT> qf;
+    WFrag<RG, MT> wf;
+    RowOut out[RG];
+    int cur_g = -1;
+    int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
+    int g_first = 0;                                  // its first global page
+    for (int j = j0; j < j1; ++j) {
+      gs = advance_group(sm.page_prefix, gs, j);
+      if (gs != cur_g) {
+        // new group: its rows, query fragments, head weights and outputs
+        // (waiting for these loads drains the page requests in flight;
+        // groups change only a few times per wave)
+        int L[RG], ql[RG];
+        bool rl[RG];
+        const GroupDesc gd = describe_group<RG>(R, sm.req_tab, gs, group_request<RG>(R, sm.req_tab, gs), L, ql, rl);
+        load_query<D, RG, MT>(p, ql, qf);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          float wv = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
+          if (!rl[r] || lane >= p.heads) wv = 0.0f;
+          wbuf[r][lane] = wv;
+          out[r] = row_out(p.logits + static_cast<int64_t>(gd.row0 + r) * p.logits_stride + gd.col0,
+                           r < gd.nrows ? L[r] : 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int hg = 4 * (lane >> 5);
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const float4 x = *reinterpret_cast<const float4*>(&wbuf[r][32 * mt + 8 * i4 + hg]);
+              wf.v[r][mt][4 * i4 + 0] = x.x;
+              wf.v[r][mt][4 * i4 + 1] = x.y;
+              wf.v[r][mt][4 * i4 + 2] = x.z;
+              wf.v[r][mt][4 * i4 + 3] = x.w;
+            }
+        g_first = sm.page_prefix[gs];
+        cur_g = gs;
+      }
+      const int nxt = j + 2 < j1 ? id_of(j + 2) : 0;
+      // page j has landed once only the requests after it (page j + 1, if
+      // any) are outstanding
+      if (j + 1 < j1) wait_all_but_last_page<D, MX>();
+      else wait_all_loads();
+      const int slot = (j - j0) & 1;
+      score_page<D, MX, RG, MT>(sm.page[wave][slot], wf, qf, out, j - g_first);
+      if (j + 2 < j1) dma_page<D, MX>(p, nxt, buf_lds[slot]);  // page j + 2 into the freed buffer
     }
   }
+  wait_all_loads();  // no request may still be writing LDS when the wave ends
 }
 
 }  // namespace idx

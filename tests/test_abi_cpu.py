@@ -171,8 +171,8 @@ def test_workspace_sizes(lib):
     c = _cache()
     r = _rows(num_req=32, max_seq_len=300)
     wsb = lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 64, 2048)
-    # header + counters (256-aligned) + 32 rows x 320 fp32 scratch
-    assert wsb == 256 + 256 + 32 * 320 * 4
+    # header + 32 rows x 320 fp32 row logits
+    assert wsb == 256 + 32 * 320 * 4
     assert lib.idx_workspace_bytes(B.IDX_OP_LOGITS, ctypes.byref(c), ctypes.byref(r), 64, 0) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, 16) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 99, 16) == 0

@@ -134,10 +134,8 @@ def test_decode_topk_workspace_reuse_and_determinism():
     out1, ws = dev.decode_topk()
     out2, _ = dev.decode_topk(ws)
     assert np.array_equal(out1, out2)
-    # completion counters are back at zero after every completed call
-    n_groups = wl.num_req
-    counters = ws[256 : 256 + 4 * n_groups].view(torch.int32).cpu().numpy()
-    assert not counters.any()
+    # the status word stays clear on valid input
+    assert int(ws[:4].view(torch.int32).cpu()[0]) == 0
     # a smaller batch reusing the same (larger) workspace
     wl2 = _case("fp8", 128, 64, 1, False, seed=10)
     dev2 = Dev(wl2)
