@@ -18,12 +18,59 @@ constexpr int kPage = 64;  // tokens per cache page
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (global_load_lds) with counted waits
+// ---------------------------------------------------------------------------
+
+// One direct global -> LDS load: lane i's `size` bytes at gptr land at LDS
+// byte address lds + size * i.  Written as inline assembly so that the
+// compiler's own wait-count tracking, which cannot tell LDS buffers
+// apart and would wait for every request before any LDS read, stays out of
+// it; the waits below count these loads instead.  (An asm load also makes any
+// wait the compiler computes for its own loads stricter, never weaker.)
+// Each load sets m0, which nothing else in this library keeps live.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is named as clobbered on purpose
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p)));
+}
+
+// s_waitcnt for vector memory only (vmcnt <= n; the gfx9 encoding keeps
+// vmcnt in bits [3:0] and [15:14] and leaves expcnt and lgkmcnt at their
+// maxima).  The builtin keeps the compiler's wait-count model in step (it
+// learns that its own older loads are complete); the empty asm keeps LDS
+// reads of the DMA'd data from moving above the wait.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_all_loads() { wait_vmcnt<0>(); }
+
 // Order-preserving map from float to uint32: larger float -> larger key.
 // -0.0 is first folded onto +0.0 so that both compare equal.
 __device__ __forceinline__ uint32_t ordered_key(float x) {
   uint32_t b = __float_as_uint(x);
   if (b == 0x80000000u) b = 0u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Number of set bits of m below this lane.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
 }
 
 // Wave-wide inclusive prefix sum (DPP: shifts within 16-lane rows, then
@@ -58,6 +105,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int& total, int* sm) 
   __syncthreads();
   total = tot;
   return before + x - v;
+}
+
+// Block-wide min / max of a float over NT threads (`sm` holds NT/64 ints).
+template <int NT>
+__device__ __forceinline__ float block_min(float v, int* sm) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v = fminf(v, __shfl_xor(v, d, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) sm[threadIdx.x / kWave] = __float_as_int(v);
+  __syncthreads();
+  float r = __int_as_float(sm[0]);
+  for (int w = 1; w < NT / kWave; ++w) r = fminf(r, __int_as_float(sm[w]));
+  __syncthreads();
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ float block_max(float v, int* sm) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) sm[threadIdx.x / kWave] = __float_as_int(v);
+  __syncthreads();
+  float r = __int_as_float(sm[0]);
+  for (int w = 1; w < NT / kWave; ++w) r = fmaxf(r, __int_as_float(sm[w]));
+  __syncthreads();
+  return r;
 }
 
 __device__ __forceinline__ int block_sum_int(int v, int* sm, int nt) {

@@ -21,7 +21,7 @@ idx_status fail(idx_status st, const char* what) {
   return st;
 }
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 
 int row_bytes(int fmt, int d) { return fmt == IDX_FMT_FP8_E4M3 ? d + 4 : d / 2 + d / 32; }
 

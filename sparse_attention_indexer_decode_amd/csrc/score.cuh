@@ -302,25 +302,6 @@ __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (
 // Direct global -> LDS page loads
 // ---------------------------------------------------------------------------
 
-// One direct global -> LDS load: lane i's `size` bytes at gptr land at LDS
-// byte address lds + size * i.  Written as inline assembly so that the
-// compiler's own wait-count tracking, which cannot tell the two ring buffers
-// apart and would wait for every request before any LDS read, stays out of
-// it; the waits below count these loads instead.  (An asm load also makes any
-// wait the compiler computes for its own loads stricter, never weaker.)
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
-}
-
-// LDS byte address of a shared-memory pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p)));
-}
-
 // Requests page `phys` into the LDS buffer at byte address `lds`: byte i of
 // the page lands at lds + i.  Always issues exactly kLoads loads.
 template <int D, bool MX>
@@ -334,20 +315,6 @@ __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_
   for (int c = 0; c < Geo::kNarrow; ++c)
     lds_dma4(src + 1024 * Geo::kWide + 256 * c + 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
 }
-
-// s_waitcnt for vector memory only (vmcnt <= n; the gfx9 encoding keeps
-// vmcnt in bits [3:0] and [15:14] and leaves expcnt and lgkmcnt at their
-// maxima).  The builtin keeps the compiler's wait-count model in step (it
-// learns that its own older loads are complete); the empty asm keeps LDS
-// reads of the DMA'd data from moving above the wait.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void wait_all_loads() { wait_vmcnt<0>(); }
 
 // Waits until at most kLoads vector-memory operations are outstanding: every
 // page requested before the most recent one has landed in LDS (vector memory

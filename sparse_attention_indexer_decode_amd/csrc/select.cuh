@@ -9,7 +9,15 @@
 // Keys: floats map to order-preserving 32-bit keys (-0.0 folded onto +0.0).
 // Digits: d1 = key[31:20] (4096 bins), then key[19:10] and key[9:0].
 //
-// Method (few dependent global round trips):
+// Rows of up to kRowCap keys (the common case) are resident in LDS:
+//   1. the whole row is requested at once with direct global->LDS loads;
+//   2. three LDS histogram passes (d1, then the two lower digits among the
+//      keys matching the prefix so far) fix the threshold key T and how many
+//      keys equal to T are taken (`need`, the lowest positions);
+//   3. ordered emission: each wave owns a run of 64-key blocks; per block a
+//      ballot of "above T" and "equal to T" gives, with the wave's running
+//      counts and one scan over the waves, every winner's output slot.
+// Longer rows stream from global memory:
 //   1. d1 histogram of the row in LDS, one pass with many coalesced loads in
 //      flight.
 //   2. The d1 bin B1 holding the k-th largest; every element with d1 >= B1
@@ -22,9 +30,10 @@
 //      a radix select on the positions themselves when T is tied); one
 //      ordered scan over the bitmap words writes the k positions in
 //      ascending order.
-// Rows whose candidates exceed LDS capacity (very many equal keys) or whose
-// length exceeds the bitmap use multi-pass global refinement and a global
-// ordered compaction instead; both paths select the same set.
+//   Rows whose candidates exceed LDS capacity (very many equal keys) or whose
+//   length exceeds the bitmap use multi-pass global refinement and a global
+//   ordered compaction instead.
+// Every path selects the same set.
 #pragma once
 
 #include "device_common.cuh"
@@ -35,16 +44,19 @@ constexpr int kD1Bins = 4096;
 constexpr int kD1Shift = 20;
 constexpr int kCandCap = 4096;
 constexpr int kBitmapWords = 4096;  // bitmap path for rows up to 131072 keys
+constexpr int kRowCap = 32768;      // keys of an LDS-resident row
 
 template <int NT>
 struct SelectShared {
-  uint32_t ckey[kCandCap];
-  int cidx[kCandCap];
+  struct {
+    uint32_t ckey[kCandCap];
+    int cidx[kCandCap];
+  } c;
   union {
     int hist1[kD1Bins];          // first-digit histogram (when not given)
     uint32_t sel[kBitmapWords];  // winners, one bit per position
   } u;
-  int hist2[1024];
+  int hist2[2048];
   int scan[NT / kWave];
   int bc[8];
 };
@@ -170,39 +182,43 @@ __device__ void row_histogram(const float* __restrict__ row, int L, bool aligned
   __syncthreads();
 }
 
-// Narrows st (prefix, pmask, need) among the elements matching st.prefix
-// under st.pmask, over two digit passes (shift, bits); `for_each(fn)`
-// visits the key of every element to consider and is called once per pass
-// by all threads.  Returns the number of elements matching the final
-// prefix (equal to st.need when the last bin examined is taken whole).
+// One radix step: among the elements whose key matches st.prefix under
+// st.pmask, histogram digit (key >> shift) & (2^bits - 1) and narrow st to
+// the digit holding the st.need-th largest.  `for_each(fn)` visits the key
+// of every element to consider and is called by all threads.  Returns the
+// number of elements in the chosen digit (equal to the updated st.need when
+// that digit is taken whole).
+template <int NT, class ForEach>
+__device__ int refine_pass(SelectState& st, int shift, int bits, ForEach for_each, SelectShared<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int nb = 1 << bits;
+  const uint32_t dmask = static_cast<uint32_t>(nb - 1);
+  for (int j = tid; j < nb; j += NT) sm.hist2[j] = 0;
+  __syncthreads();
+  const uint32_t prefix = st.prefix, pmask = st.pmask;
+  for_each([&](uint32_t key) {
+    if ((key & pmask) == prefix) atomicAdd(&sm.hist2[(key >> shift) & dmask], 1);
+  });
+  __syncthreads();
+  int digit, above, cnt;
+  if (nb >= NT) {
+    find_digit<NT>(nb, st.need, [&](int d) { return sm.hist2[d]; }, sm, digit, above, cnt);
+  } else {
+    // fewer bins than threads: pad the digit space to NT bins
+    find_digit<NT>(NT, st.need, [&](int d) { return d < nb ? sm.hist2[d] : 0; }, sm, digit, above, cnt);
+  }
+  st.prefix |= static_cast<uint32_t>(digit) << shift;
+  st.pmask |= dmask << shift;
+  st.need -= above;
+  return cnt;
+}
+
+// Two radix steps (the second skipped when the first digit is taken whole).
 template <int NT, class ForEach>
 __device__ int refine(SelectState& st, int shift0, int bits0, int shift1, int bits1, ForEach for_each,
                       SelectShared<NT>& sm) {
-  const int tid = threadIdx.x;
-  int cnt = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? shift0 : shift1;
-    const int nb = 1 << (pass == 0 ? bits0 : bits1);
-    const uint32_t dmask = static_cast<uint32_t>(nb - 1);
-    for (int j = tid; j < nb; j += NT) sm.hist2[j] = 0;
-    __syncthreads();
-    const uint32_t prefix = st.prefix, pmask = st.pmask;
-    for_each([&](uint32_t key) {
-      if ((key & pmask) == prefix) atomicAdd(&sm.hist2[(key >> shift) & dmask], 1);
-    });
-    __syncthreads();
-    int digit, above;
-    if (nb >= NT) {
-      find_digit<NT>(nb, st.need, [&](int d) { return sm.hist2[d]; }, sm, digit, above, cnt);
-    } else {
-      // fewer bins than threads: pad the digit space to NT bins
-      find_digit<NT>(NT, st.need, [&](int d) { return d < nb ? sm.hist2[d] : 0; }, sm, digit, above, cnt);
-    }
-    st.prefix |= static_cast<uint32_t>(digit) << shift;
-    st.pmask |= dmask << shift;
-    st.need -= above;
-    if (st.need == cnt) break;  // the whole bin is taken
-  }
+  int cnt = refine_pass<NT>(st, shift0, bits0, for_each, sm);
+  if (st.need != cnt) cnt = refine_pass<NT>(st, shift1, bits1, for_each, sm);
   return cnt;
 }
 
@@ -250,16 +266,11 @@ __device__ void compact_global(const float* __restrict__ row, int L, int k, bool
   }
 }
 
-// Top-k of one row (kept out of line: it runs once per row, and inlining it
-// would raise the scorer's register pressure).
+// Top-k of a row streamed from global memory (k < L).
 template <int NT>
-__device__ __noinline__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out,
-                                        SelectShared<NT>& sm) {
+__device__ void select_row_stream(const float* __restrict__ row, int L, int k, int* __restrict__ out,
+                                  SelectShared<NT>& sm) {
   const int tid = threadIdx.x;
-  if (L <= k) {
-    for (int j = tid; j < k; j += NT) out[j] = (j < L) ? j : -1;
-    return;
-  }
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
 
   // 1. first digit
@@ -314,8 +325,8 @@ __device__ __noinline__ void select_row(const float* __restrict__ row, int L, in
       for (int j = 0; j < 4 * V; ++j) {
         if (v[j] && u[j] >= lo_key) {
           if (pos < kCandCap) {
-            sm.ckey[pos] = u[j];
-            sm.cidx[pos] = strided_pos<NT>(base, j);
+            sm.c.ckey[pos] = u[j];
+            sm.c.cidx[pos] = strided_pos<NT>(base, j);
           }
           ++pos;
         }
@@ -329,7 +340,7 @@ __device__ __noinline__ void select_row(const float* __restrict__ row, int L, in
   int n_eq = cnt1;
   if (st.need != cnt1) {
     n_eq = refine<NT>(st, 10, 10, 0, 10, [&](auto fn) {
-      for (int i = tid; i < nc; i += NT) fn(sm.ckey[i]);
+      for (int i = tid; i < nc; i += NT) fn(sm.c.ckey[i]);
     }, sm);
   }
 
@@ -339,8 +350,8 @@ __device__ __noinline__ void select_row(const float* __restrict__ row, int L, in
   __syncthreads();
   const bool take_all_eq = st.need == n_eq;
   for (int i = tid; i < nc; i += NT) {
-    const uint32_t m = sm.ckey[i] & st.pmask;
-    const int p = sm.cidx[i];
+    const uint32_t m = sm.c.ckey[i] & st.pmask;
+    const int p = sm.c.cidx[i];
     if (m > st.prefix || (take_all_eq && m == st.prefix)) atomicOr(&sm.u.sel[p >> 5], 1u << (p & 31));
   }
   if (!take_all_eq) {
@@ -350,11 +361,11 @@ __device__ __noinline__ void select_row(const float* __restrict__ row, int L, in
     SelectState ts{0u, 0u, st.need};
     refine<NT>(ts, 8, 9, 0, 8, [&](auto fn) {
       for (int i = tid; i < nc; i += NT)
-        if ((sm.ckey[i] & tmask) == tprefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.cidx[i]));
+        if ((sm.c.ckey[i] & tmask) == tprefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.c.cidx[i]));
     }, sm);
     for (int i = tid; i < nc; i += NT) {
-      const int p = sm.cidx[i];
-      if ((sm.ckey[i] & tmask) == tprefix && (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix)
+      const int p = sm.c.cidx[i];
+      if ((sm.c.ckey[i] & tmask) == tprefix && (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix)
         atomicOr(&sm.u.sel[p >> 5], 1u << (p & 31));
     }
   }
@@ -377,6 +388,183 @@ __device__ __noinline__ void select_row(const float* __restrict__ row, int L, in
     }
   }
   __syncthreads();
+}
+
+// Top-k of a row held in registers (k < L <= kRowCap).  Thread t holds
+// keys t + NT j, j < E.  The first digit is linear in the value between the
+// row's minimum and maximum (monotone, so any such digit works), which
+// spreads the keys over the 4096 bins instead of crowding them into the few
+// exponent bins the key's top bits would give; the exact 32-bit key only
+// decides within the threshold bin.
+template <int NT, int E>
+__device__ void select_row_reg(const float* __restrict__ row, int L, int k, int* __restrict__ out,
+                               SelectShared<NT>& sm) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int nj = (L + NT - 1) / NT;  // register slots in use (uniform)
+
+  // 1. load: all loads in flight at once
+  float x[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int p = tid + NT * j;
+    if (j < nj) x[j] = row[p < L ? p : L - 1];
+  }
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < nj) {
+      lo = fminf(lo, x[j]);
+      hi = fmaxf(hi, x[j]);
+    }
+  }
+  for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
+  lo = block_min<NT>(lo, sm.scan);
+  hi = block_max<NT>(hi, sm.scan);
+  // bin(v) = clamp(fma(v, a, b), 0, 4095) truncated, with a = 4096 / (hi - lo)
+  // and b = -lo a: one rounding of (v - lo) a, so monotone non-decreasing in
+  // v.  (hi - lo is formed from halves so that it cannot overflow; when a or
+  // b is not finite every key goes to bin 0, which is slow but still exact.)
+  const float half_range = hi * 0.5f - lo * 0.5f;
+  float a = half_range > 0.0f ? static_cast<float>(kD1Bins / 2) / half_range : 0.0f;
+  float b = -(lo * a);
+  if (!(__builtin_fabsf(a) <= 3.0e38f) || !(__builtin_fabsf(b) <= 3.0e38f)) a = b = 0.0f;
+  auto bin_of = [&](float v) -> int {
+    return static_cast<int>(__builtin_amdgcn_fmed3f(__builtin_fmaf(v, a, b), 0.0f, static_cast<float>(kD1Bins - 1)));
+  };
+
+  // 2. first-digit histogram and the bin B1 holding the k-th largest
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < nj && tid + NT * j < L) atomicAdd(&sm.u.hist1[bin_of(x[j])], 1);
+  }
+  __syncthreads();
+  int B1, above1, cnt1;
+  find_digit<NT>(kD1Bins, k, [&](int d) { return sm.u.hist1[d]; }, sm, B1, above1, cnt1);
+  const int n_cand = above1 + cnt1;
+  if (n_cand > kCandCap) {
+    // too many keys at or above B1 (large ties): radix-select from global
+    select_row_stream<NT>(row, L, k, out, sm);
+    return;
+  }
+
+  // 3. candidates (bin >= B1) -> (key, position) list: per-wave counts,
+  //    their prefix over the waves, then ordered writes within each wave
+  int c_own = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < nj) c_own += __popcll(__ballot(tid + NT * j < L && bin_of(x[j]) >= B1));
+  }
+  if (lane == 0) sm.scan[wave] = c_own;
+  __syncthreads();
+  int pos = 0;
+  for (int w = 0; w < wave; ++w) pos += sm.scan[w];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < nj) {
+      const int p = tid + NT * j;
+      const int b = bin_of(x[j]);
+      const bool c = p < L && b >= B1;
+      const uint64_t m = __ballot(c);
+      if (c) {
+        const int slot = pos + mbcnt64(m);
+        // above-bin candidates carry key 0xFFFFFFFF: they always win
+        sm.c.ckey[slot] = b > B1 ? 0xFFFFFFFFu : ordered_key(x[j]);
+        sm.c.cidx[slot] = p;
+      }
+      pos += __popcll(m);
+    }
+  }
+  __syncthreads();
+  const int nc = n_cand;
+
+  // 4. exact threshold key among the candidates of bin B1 (need = k - above1)
+  SelectState st{0u, 0u, k - above1};
+  int n_eq = cnt1;
+  if (st.need != cnt1) {
+    auto in_bin = [&](auto fn) {
+      for (int i = tid; i < nc; i += NT) {
+        const uint32_t key = sm.c.ckey[i];
+        if (key != 0xFFFFFFFFu) fn(key);
+      }
+    };
+    n_eq = refine_pass<NT>(st, 21, 11, in_bin, sm);
+    if (st.need != n_eq) n_eq = refine_pass<NT>(st, 10, 11, in_bin, sm);
+    if (st.need != n_eq) n_eq = refine_pass<NT>(st, 0, 10, in_bin, sm);
+  } else {
+    st.pmask = 0u;  // bin B1 taken whole: every candidate wins
+    n_eq = nc;
+    st.need = nc;
+  }
+  // winners: key 0xFFFFFFFF (above B1), in-bin keys with (key & pmask) >
+  // prefix, and of those equal under pmask the `need` lowest positions
+
+  // 5. winners -> position bitmap
+  uint32_t* bits = sm.u.sel;
+  const int W = (L + 31) >> 5;
+  for (int j = tid; j < W; j += NT) bits[j] = 0u;
+  __syncthreads();
+  const bool take_all_eq = st.need == n_eq;
+  const uint32_t prefix = st.prefix, pmask = st.pmask;
+  for (int i = tid; i < nc; i += NT) {
+    const uint32_t key = sm.c.ckey[i];
+    const int p = sm.c.cidx[i];
+    const uint32_t m = key & pmask;
+    const bool above = key == 0xFFFFFFFFu && pmask != 0u;
+    if (above || m > prefix || (take_all_eq && m == prefix)) atomicOr(&bits[p >> 5], 1u << (p & 31));
+  }
+  if (!take_all_eq) {
+    // equal keys at the threshold: the `need` lowest positions among them,
+    // i.e. the largest of (2^17 - 1 - position), by radix select on 17 bits
+    SelectState ts{0u, 0u, st.need};
+    auto tied = [&](auto fn) {
+      for (int i = tid; i < nc; i += NT) {
+        const uint32_t key = sm.c.ckey[i];
+        if (key != 0xFFFFFFFFu && (key & pmask) == prefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.c.cidx[i]));
+      }
+    };
+    refine<NT>(ts, 8, 9, 0, 8, tied, sm);
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t key = sm.c.ckey[i];
+      const int p = sm.c.cidx[i];
+      if (key != 0xFFFFFFFFu && (key & pmask) == prefix && (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix)
+        atomicOr(&bits[p >> 5], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+
+  // 6. ordered emission: thread t owns bitmap words [t wpt, (t + 1) wpt)
+  const int wpt = (W + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  const int w1 = (w0 + wpt < W) ? w0 + wpt : W;
+  int c_sel = 0;
+  for (int wd = w0; wd < w1; ++wd) c_sel += __popc(bits[wd]);
+  int tot;
+  int o = block_exclusive_scan<NT>(c_sel, tot, sm.scan);
+  for (int wd = w0; wd < w1; ++wd) {
+    uint32_t sel = bits[wd];
+    while (sel) {
+      const int bpos = __builtin_ctz(sel);
+      sel &= sel - 1u;
+      out[o++] = wd * 32 + bpos;
+    }
+  }
+  __syncthreads();
+  (void)NW;
+}
+
+// Top-k of one row.
+template <int NT>
+__device__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out, SelectShared<NT>& sm) {
+  if (L <= k) {
+    for (int j = threadIdx.x; j < k; j += NT) out[j] = (j < L) ? j : -1;
+  } else if (L <= kRowCap) {
+    select_row_reg<NT, kRowCap / NT>(row, L, k, out, sm);
+  } else {
+    select_row_stream<NT>(row, L, k, out, sm);
+  }
 }
 
 }  // namespace idx

@@ -71,20 +71,34 @@ def test_c1_tiny_decode():
 
 
 def _topk_rows(k):
+    """Rows of every length class the selector distinguishes (empty, L <= k,
+    register-resident up to 32768, streamed beyond) and value patterns that
+    stress its digits: ties, signed zeros, one value, huge and infinite
+    magnitudes, subnormals, 60 decades of range, tied levels at the top."""
     rng = np.random.default_rng(5)
-    lens = [0, 1, k - 1, k, k + 1, 100, 1000, 5000, 33000, 131072]
+    lens = [0, 1, k - 1, k, k + 1, 100, 1000, 5000, 33000, 131072, 3000, 20000, 32768, 32769, 9000, 12000]
     rows = []
     for i, L in enumerate(lens):
-        kind = i % 4
+        kind = i % 8
         if kind == 0:
             v = rng.standard_normal(L).astype(np.float32) * 8
         elif kind == 1:
             v = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0], dtype=np.float32), size=L)
         elif kind == 2:
             v = np.full(L, 3.25, dtype=np.float32)
-        else:
+        elif kind == 3:
             v = (rng.integers(-3, 4, size=L) * 0.125).astype(np.float32)
             v[::7] = -0.0
+        elif kind == 4:
+            v = np.clip(rng.standard_normal(L) * 1e38, -3.3e38, 3.3e38).astype(np.float32)
+            v[::97] = np.inf
+            v[5::89] = -np.inf
+        elif kind == 5:
+            v = (rng.standard_normal(L) * 1e-40).astype(np.float32)   # subnormals
+        elif kind == 6:
+            v = (rng.choice([-1.0, 1.0], size=L) * 10.0 ** rng.uniform(-30, 30, size=L)).astype(np.float32)
+        else:
+            v = (rng.integers(0, 50, size=L) * 0.1).astype(np.float32)
         rows.append(v)
     return lens, rows
 
