@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused decode indexer (scoring + top-k) on one MI355X.
+"""Benchmark of the decode indexer (scoring + top-k) on one MI355X.
 
 Workload: the fp8 decode batch -- 32 requests, seq_len ~ U[4096, 32768],
 page 64, 20,000-page pool, H=64 index heads, head_dim 128, top-k 2048,
-next_n=1 (synthetic, seeded).  A step is one idx_decode_topk call over the
-whole batch: row expansion, page gather, bf16-MFMA scoring with the
-ReLU-weighted head sum, and the fused top-k.
+next_n=1 (synthetic, seeded).  A step is the whole decode path over the
+batch: row expansion, page gather, bf16-MFMA scoring with the ReLU-weighted
+head sum (idx_logits_paged), then the per-row top-k (idx_topk) -- the same
+two launches idx_decode_topk makes, called separately so that HIP events
+between them time the scorer on its own.
 
 Timing: inputs are resident in HBM before the timed region.  The pool
 (169 MB) would fit the 256 MiB MALL, so each step reads one of `--copies`
@@ -34,8 +36,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "index keys scored/sec + top-k rows/sec, 1×MI355X; % of HBM (decode) / MFMA (prefill) peak"
 HBM_PEAK_GBS = 8000.0
-PROFILE_NAME = "decode_fused_fp8_c2"
-KERNEL_SUBSTR = "score_kernelILi128ELb0ELi1ELi2ELb1E"   # fused decode, D=128, fp8, 1 row/group, 64 heads
+PROFILE_NAME = "score_kernel_fp8_decode_32req"
+KERNEL_SUBSTR = "score_kernelILi128ELb0ELi1ELi2EE"   # scorer: D=128, fp8, 1 row/group, 64 heads
+TOPK_SUBSTR = "topk_kernel"
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
 
 
@@ -48,19 +51,20 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Bytes one fused decode launch must move at minimum: every live key
-    row once (D codes + 4-byte scale), each row's bf16 q and fp32 w, the
-    block-table entries of the live pages, the lengths, and the top-k out."""
+    """Bytes one scorer launch must move at minimum: every live key row once
+    (D fp8 codes + 4-byte scale = 132 B at D=128), one fp32 logit written per
+    key (4 B), each row's bf16 q and fp32 w, the block-table entries of the
+    live pages and the lengths."""
     keys = int(wl.seq_lens.astype("int64").sum())
     rows = wl.num_req * wl.next_n
     pages = int(sum(-(-int(L) // 64) for L in wl.seq_lens))
     b = {
         "keys": keys * wl.row_bytes,
+        "logits": keys * 4,
         "q": rows * wl.heads * wl.head_dim * 2,
         "w": rows * wl.heads * 4,
         "block_table": pages * 4,
         "lengths": wl.num_req * 4,
-        "out": rows * wl.topk * 4,
     }
     b["total"] = sum(b.values())
     return b
@@ -141,10 +145,20 @@ def run(args):
     R = rows.num_rows
     outs = torch.empty((R, k), dtype=torch.int32, device=dev)
     ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, caches[0], rows, wl.heads, k), dev)
+    ML = int(wl.seq_lens.max())
+    stride = -(-ML // 64) * 64
+    logits = torch.empty((R, stride), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        idx.idx_decode_topk(caches[i % len(caches)], rows, q, w, k, outs, ws, stream)
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        idx.idx_logits_paged(caches[i % len(caches)], rows, q, w, logits, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        idx.idx_topk(logits, rows, k, outs, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     if args.calib:
         # a plain elementwise copy of known size (reads and writes calib_mib
@@ -159,36 +173,39 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
     first = outs.clone()
+    # the public one-call entry point makes the same two launches
+    fused = torch.full_like(outs, -7)
+    idx.idx_decode_topk(caches[0], rows, q, w, k, fused, ws, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(first, fused), "idx_decode_topk differs from idx_logits_paged + idx_topk"
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        step(args.warmup + i)
-        ends[i].record(stream)
+        step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    assert torch.equal(first, outs), "fused decode is not deterministic across steps"
+    score_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    assert torch.equal(first, outs), "decode top-k is not deterministic across steps"
 
     # warm-MALL reference: the same pool back to back (context only)
     for _ in range(5):
-        idx.idx_decode_topk(caches[0], rows, q, w, k, outs, ws, stream)
+        step(0)
     ws_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ws_ev[0].record(stream)
     for _ in range(20):
-        idx.idx_decode_topk(caches[0], rows, q, w, k, outs, ws, stream)
+        step(0)
     ws_ev[1].record(stream)
     torch.cuda.synchronize()
     warm_ms = ws_ev[0].elapsed_time(ws_ev[1]) / 20
 
     keys_scored = scored_keys(wl)
     ms_per_step = wall * 1000.0 / args.steps
-    launch_avg_ms = float(np.mean(launch_ms))
+    score_avg_ms = float(np.mean(score_ms))
     ab = algorithmic_bytes(wl)
-    achieved = ab["total"] / (launch_avg_ms * 1e-3) / 1e9
+    achieved = ab["total"] / (score_avg_ms * 1e-3) / 1e9
     traffic, prof = load_traffic(ab["total"])
     res = {
         "metric": METRIC,
@@ -208,13 +225,14 @@ def run(args):
                    "name": wl.name, "requests": wl.num_req, "rows": R, "keys_scored": keys_scored,
                    "cache_fmt": "fp8_e4m3", "pool_copies_rotated": args.copies},
         "rows_per_s": R / (ms_per_step * 1e-3),
-        "launch_ms_avg": launch_avg_ms,
-        "launch_ms_min": float(np.min(launch_ms)),
+        "scorer_ms_avg": score_avg_ms,
+        "scorer_ms_min": float(np.min(score_ms)),
+        "topk_ms_avg": float(np.mean(topk_ms)),
         "warm_mall_ms_per_step": warm_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["total"],
-                     "kernel": "score_kernel<128, fp8, 1, 2, fused>"},
+                     "kernel": "score_kernel<D=128, fp8, 1 row/group, 64 heads> (idx_logits_paged)"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
@@ -287,12 +305,12 @@ def summarize(dirs, commands):
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", PROFILE_NAME + ".json"), "w") as f:
         json.dump(out, f, indent=1)
-    md = [f"# Fused decode indexer, fp8 decode batch (32 x U[4096, 32768], H=64, D=128, k=2048)", "",
+    md = [f"# Scorer kernel on the fp8 decode batch (32 x U[4096, 32768], H=64, D=128, k=2048)", "",
           "Commands (run from the repository root on one MI355X):", ""]
     md += [f"    {c}" for c in commands]
     md += ["", "## rocprofv3 --kernel-trace --stats", "",
            "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"] + lines
-    md += ["", "## HBM traffic of the fused kernel (rocprofv3 --pmc, per dispatch)", "",
+    md += ["", "## HBM traffic of the scorer kernel (rocprofv3 --pmc, per dispatch)", "",
            f"- FETCH_SIZE {out['fetch_kib_per_launch']} KiB, WRITE_SIZE {out['write_kib_per_launch']} KiB",
            f"- plain 256 MiB copy reads as FETCH {out['copy_fetch_kib']} KiB / WRITE {out['copy_write_kib']} KiB "
            f"-> scale {f_scale:.4f} / {w_scale:.4f}",

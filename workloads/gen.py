@@ -72,40 +72,47 @@ _E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64
 
 def _e2m1_code(mag: np.ndarray) -> np.ndarray:
     """Magnitudes (already divided by the block scale) -> 3-bit e2m1 codes,
-    round to nearest, ties to the even code, saturating at 6."""
+    round to nearest, ties to the even code, saturating at 6.
+
+    The grid is 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7).  The code is the
+    number of midpoints below the magnitude; a magnitude exactly on the
+    midpoint between codes i and i+1 rounds up only when i+1 is even."""
     mag = np.minimum(mag, 6.0)
-    # distance to every grid point; pick the nearest, ties -> even code
-    dist = np.abs(mag[..., None] - _E2M1_GRID)
-    best = dist.min(axis=-1, keepdims=True)
-    cand = dist == best
-    # prefer even code index among ties
-    even = cand & (np.arange(8) % 2 == 0)
-    pick_even = even.any(axis=-1)
-    code = np.where(pick_even, even.argmax(axis=-1), cand.argmax(axis=-1))
-    return code.astype(np.uint8)
+    mids = ((_E2M1_GRID[:-1] + _E2M1_GRID[1:]) * 0.5).astype(mag.dtype)
+    code = np.zeros(mag.shape, dtype=np.uint8)
+    for i, m in enumerate(mids):
+        up = (mag >= m) if (i + 1) % 2 == 0 else (mag > m)
+        code += up.view(np.uint8)
+    return code
 
 
 def encode_mxfp4_rows(k: np.ndarray) -> np.ndarray:
     """fp32 keys [n, D] -> token rows [n, D/2 + D/32] in the OCP MX FP4 form:
     per 32-element block a shared power-of-two scale 2^(floor(log2 amax) - 2),
-    elements rounded to e2m1 (nearest, ties to even, saturating)."""
+    elements rounded to e2m1 (nearest, ties to even, saturating).  (Bulk
+    arithmetic on torch CPU tensors; every step is exact in fp32.)"""
     k = np.ascontiguousarray(k, dtype=np.float32)
     n, d = k.shape
     assert d % 32 == 0
     nb = d // 32
-    blocks = k.reshape(n, nb, 32).astype(np.float64)
-    amax = np.abs(blocks).max(axis=2)
-    with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
-    e = np.clip(e, -127, 127).astype(np.int32)
-    scaled = blocks / np.exp2(e.astype(np.float64))[..., None]
-    code = _e2m1_code(np.abs(scaled))
+    blocks = torch.from_numpy(k).view(n, nb, 32)
+    amax = blocks.abs().amax(dim=2)
+    # floor(log2 amax) from the binary exponent (frexp: amax = m 2^ex, m in [.5, 1))
+    _, ex = torch.frexp(amax)
+    e = torch.where(amax > 0, ex.to(torch.int32) - 3, torch.full_like(ex, -127, dtype=torch.int32))
+    e = e.clamp(-127, 127)
+    scaled = blocks * torch.ldexp(torch.ones_like(amax), -e).unsqueeze(-1)   # exact: power of two
+    mag = scaled.abs().clamp(max=6.0)
+    code = torch.zeros(mag.shape, dtype=torch.uint8)
+    for i, m in enumerate(((_E2M1_GRID[:-1] + _E2M1_GRID[1:]) * 0.5).tolist()):
+        # midpoint between codes i and i+1: ties go up only to an even code
+        code += (mag >= m) if (i + 1) % 2 == 0 else (mag > m)
     sign = (scaled < 0) & (code > 0)
-    nib = (code | (sign.astype(np.uint8) << 3)).reshape(n, d)
-    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    nib = (code | (sign.to(torch.uint8) << 3)).view(n, d)
+    packed = nib[:, 0::2] | (nib[:, 1::2] << 4)
     out = np.empty((n, d // 2 + nb), dtype=np.uint8)
-    out[:, : d // 2] = packed
-    out[:, d // 2 :] = (e + 127).astype(np.uint8)
+    out[:, : d // 2] = packed.numpy()
+    out[:, d // 2 :] = (e + 127).to(torch.uint8).numpy()
     return out
 
 
