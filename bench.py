@@ -37,8 +37,9 @@ sys.path.insert(0, ROOT)
 METRIC = "index keys scored/sec + top-k rows/sec, 1×MI355X; % of HBM (decode) / MFMA (prefill) peak"
 HBM_PEAK_GBS = 8000.0
 PROFILE_NAME = "score_kernel_fp8_decode_32req"
-KERNEL_SUBSTR = "score_kernelILi128ELb0ELi1ELi2EE"   # scorer: D=128, fp8, 1 row/group, 64 heads
-TOPK_SUBSTR = "topk_kernel"
+KERNEL_SUBSTR = "score_kernel<128, false, 1, 2>"   # scorer: D=128, fp8, 1 row/group, 64 heads
+TOPK_SUBSTR = "topk_kernel<"
+CALIB_SUBSTR = "AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float>"
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
 
 
@@ -82,9 +83,10 @@ def scored_keys(wl) -> int:
     return total
 
 
-def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
-    """The oracle (numpy, float64) on the host cores, on as many whole
-    requests as fit in about `budget_s` seconds."""
+def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
+    """The oracle (numpy, float64) on the host cores: whole requests of the
+    batch in order, cycling over the batch, until about `budget_s` seconds
+    of work are done."""
     import numpy as np
     import oracle
 
@@ -96,17 +98,17 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     keys = 0
     t0 = time.perf_counter()
     done = 0
-    for b in range(wl.num_req):
+    while time.perf_counter() - t0 < budget_s:
+        b = done % wl.num_req
         lg = oracle.pipeline.decode_logits(wl, requests=[b])
         oracle.pipeline.decode_topk(wl, lg, requests=[b])
         keys += int(sum(len(v) for v in lg.values() if len(v) > wl.topk))
         done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
     dt = time.perf_counter() - t0
     return {"value": keys / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {wl.num_req} requests ({keys} keys, {dt:.1f} s), logits + top-k, "
-                      f"cpus visible {len(os.sched_getaffinity(0))}"}
+            "sample": f"{done} requests of the {wl.num_req}-request batch in order, cycling "
+                      f"({done / wl.num_req:.1f} passes, {keys} keys, {dt:.1f} s): dequantise, fp64 logits, "
+                      f"top-k; cpus visible {len(os.sched_getaffinity(0))}"}
 
 
 def load_traffic(per_launch_bytes: int):
@@ -249,7 +251,7 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize(dirs, commands):
+def summarize(dirs, commands, bench_json=None):
     """dirs: rocprofv3 output dirs of (1) --kernel-trace --stats, (2) --pmc
     FETCH_SIZE, (3) --pmc WRITE_SIZE runs of this script."""
     import numpy as np
@@ -267,6 +269,9 @@ def summarize(dirs, commands):
             out["avg_ns"] = float(r["AverageNs"])
             out["min_ns"] = float(r["MinNs"])
             out["max_ns"] = float(r["MaxNs"])
+        if TOPK_SUBSTR in r["Name"]:
+            out["topk_kernel"] = r["Name"]
+            out["topk_avg_ns"] = float(r["AverageNs"])
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
 
@@ -280,10 +285,16 @@ def summarize(dirs, commands):
             name = r.get("Kernel_Name", "")
             if KERNEL_SUBSTR in name:
                 per_kernel.append(v)
-            elif "copy" in name.lower() or "elementwise" in name.lower():
+            elif CALIB_SUBSTR in name:
                 copy_vals.append(v)
         return per_kernel, copy_vals
 
+    bl = None
+    if bench_json:
+        with open(bench_json) as f:
+            bl = json.loads(f.read().strip().splitlines()[-1])
+        out["bench_scorer_ms_avg"] = bl["scorer_ms_avg"]
+        out["bench_topk_ms_avg"] = bl["topk_ms_avg"]
     wl = config("C2")
     ab = algorithmic_bytes(wl)
     fetch, fcopy = counter(dirs[1], "FETCH_SIZE")
@@ -310,6 +321,14 @@ def summarize(dirs, commands):
     md += [f"    {c}" for c in commands]
     md += ["", "## rocprofv3 --kernel-trace --stats", "",
            "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"] + lines
+    if bl is not None:
+        md += ["", "## HIP-event launch durations in the same benchmark (bench.py, 200 timed steps)", "",
+               f"- scorer {bl['scorer_ms_avg'] * 1e3:.2f} us per launch (rocprofv3 kernel time "
+               f"{out.get('avg_ns', float('nan')) / 1e3:.2f} us; the events also hold the dispatch of the launch)",
+               f"- selector {bl['topk_ms_avg'] * 1e3:.2f} us per launch (rocprofv3 "
+               f"{out.get('topk_avg_ns', float('nan')) / 1e3:.2f} us)",
+               f"- step {bl['ms_per_step'] * 1e3:.2f} us wall clock; {bl['value']:.4g} keys/s; scorer "
+               f"{bl['roofline']['achieved']:.0f} GB/s algorithmic = {bl['roofline']['frac'] * 100:.1f} % of 8 TB/s"]
     md += ["", "## HBM traffic of the scorer kernel (rocprofv3 --pmc, per dispatch)", "",
            f"- FETCH_SIZE {out['fetch_kib_per_launch']} KiB, WRITE_SIZE {out['write_kib_per_launch']} KiB",
            f"- plain 256 MiB copy reads as FETCH {out['copy_fetch_kib']} KiB / WRITE {out['copy_write_kib']} KiB "
@@ -329,14 +348,15 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib", action="store_true", help="also run a plain copy for counter scaling")
     ap.add_argument("--calib-mib", type=int, default=256)
     ap.add_argument("--summarize-prof", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--bench-json", default=None)
     args = ap.parse_args()
     if args.summarize_prof:
-        summarize(args.summarize_prof, args.commands)
+        summarize(args.summarize_prof, args.commands, args.bench_json)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (multi-GPU sharding is "
