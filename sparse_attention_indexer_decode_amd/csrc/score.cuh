@@ -347,8 +347,28 @@ __device__ __forceinline__ RowOut row_out(float* base, int L) {
   return __builtin_amdgcn_make_buffer_rsrc(u, 0, n, 0x00020000);
 }
 
+// Weighted ReLU head sum of one accumulator tile into four partial sums
+// (independent chains, so the FMAs do not wait on each other).
+template <int RG, int MT>
+__device__ __forceinline__ void head_sum(const v16f& acc, const WFrag<RG, MT>& wf, int r, int mt, float (&ps)[4]) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ps[v % 4] += wf.v[r][mt][v] * relu(acc[v]);
+}
+
+// Logit of this lane's key from its four partial sums: add the other lane
+// half's heads (v_permlane32_swap leaves lo + hi in both halves), times the
+// fp8 token scale; stored through the row's buffer descriptor.
+__device__ __forceinline__ void finish_key(const float (&ps)[4], float key_scale, const RowOut& out, int off) {
+  const float partial = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(partial), __float_as_uint(partial), false, false);
+  const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * key_scale;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out, off, 0, 0);
+}
+
 // Scores the 64 keys of the page in LDS for every row of the group and
-// stores logit t = 64 pg + key of each.
+// stores logit t = 64 pg + key of each.  The MFMAs of the second 32-key tile
+// are issued before the head sums of the first, so that those VALU sums run
+// while the matrix core works.
 template <int D, bool MX, int RG, int MT>
 __device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, MT>& wf, const QFrag<D, RG, MT>& qf,
                                            const RowOut (&out)[RG], int pg) {
@@ -359,29 +379,29 @@ __device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, M
   const int n = lane & 31;
   const int g = lane >> 5;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int key = nt * 32 + n;
-    const uint8_t* rowp = buf + key * RB;
-    v8bf bfr[KS];
-    key_fragments<D, MX>(rowp, g, bfr);
-    const float key_scale = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
-    const int off = g == 0 ? (pg * kPage + key) * 4 : 0x7FFFFFF0;
+  for (int r = 0; r < RG; ++r) {
+    v16f acc[2][MT];
+    float key_scale[2];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      float partial = 0.0f;
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint8_t* rowp = buf + (nt * 32 + n) * RB;
+      v8bf bfr[KS];
+      key_fragments<D, MX>(rowp, g, bfr);
+      key_scale[nt] = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        v16f acc = {};
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v16f{};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc, 0, 0, 0);
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) partial += wf.v[r][mt][v] * relu(acc[v]);
-      }
-      // add the other lane half's heads (v_permlane32_swap: both halves end
-      // up holding lo + hi)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(partial), __float_as_uint(partial), false, false);
-      const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * key_scale;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out[r], off, 0, 0);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc[nt][mt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) head_sum<RG, MT>(acc[nt][mt], wf, r, mt, ps);
+      finish_key(ps, key_scale[nt], out[r], g == 0 ? (pg * kPage + nt * 32 + n) * 4 : 0x7FFFFFF0);
     }
   }
 }
@@ -422,6 +442,43 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
   const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
   if (!ok) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, 1u);
   return ok ? id : 0;
+}
+
+// A group's rows, query fragments, head weights (through the wave's LDS
+// staging row, into the accumulator layout) and output descriptors.
+template <int D, int RG, int MT>
+__device__ __forceinline__ void setup_group(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
+                                            float (*wbuf)[kMaxHeads], QFrag<D, RG, MT>& qf, WFrag<RG, MT>& wf,
+                                            RowOut (&out)[RG]) {
+  const RowArgs& R = p.rows;
+  const int lane = lane_id();
+  int L[RG], ql[RG];
+  bool rl[RG];
+  const GroupDesc gd = describe_group<RG>(R, req_tab, g, group_request<RG>(R, req_tab, g), L, ql, rl);
+  load_query<D, RG, MT>(p, ql, qf);
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    float wv = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
+    if (!rl[r] || lane >= p.heads) wv = 0.0f;
+    wbuf[r][lane] = wv;
+    out[r] = row_out(p.logits + static_cast<int64_t>(gd.row0 + r) * p.logits_stride + gd.col0,
+                     r < gd.nrows ? L[r] : 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int hg = 4 * (lane >> 5);
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 x = *reinterpret_cast<const float4*>(&wbuf[r][32 * mt + 8 * i4 + hg]);
+        wf.v[r][mt][4 * i4 + 0] = x.x;
+        wf.v[r][mt][4 * i4 + 1] = x.y;
+        wf.v[r][mt][4 * i4 + 2] = x.z;
+        wf.v[r][mt][4 * i4 + 3] = x.w;
+      }
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <int D, bool MX, int RG, int MT>
@@ -469,8 +526,8 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
 
   if (j0 < j1) {
     // Page ids come in batches of 64 (lane i: page jb + i), so that no
-    // compiler-visible load sits between page requests; each batch costs one
-    // drain of the requests in flight.
+    // compiler-visible load sits between page requests; a later batch costs
+    // one drain of the requests in flight.
     int jb = j0;
     int ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
     auto id_of = [&](int j) -> int {  // j < j1
@@ -480,50 +537,31 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       }
       return __builtin_amdgcn_readlane(ids, j - jb);
     };
+
+    // The first group's queries and weights are loaded together with the
+    // ids and before any page is requested: waiting for them then never
+    // waits for a page, and the first page can be scored as soon as it lands.
+    QFrag<D, RG, MT> qf;
+    WFrag<RG, MT> wf;
+    RowOut out[RG];
+    int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
+    int g_first = 0;                                  // its first global page
+    setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out);
+    g_first = sm.page_prefix[gs];
+    int cur_g = gs;
+
     const int id0 = id_of(j0);
     const int id1 = j0 + 1 < j1 ? id_of(j0 + 1) : 0;
     wait_all_loads();  // nothing the compiler loaded before is still in flight
     dma_page<D, MX>(p, id0, buf_lds[0]);
     if (j0 + 1 < j1) dma_page<D, MX>(p, id1, buf_lds[1]);
 
-    QFrag<D, RG, MT> qf;
-    WFrag<RG, MT> wf;
-    RowOut out[RG];
-    int cur_g = -1;
-    int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
-    int g_first = 0;                                  // its first global page
     for (int j = j0; j < j1; ++j) {
       gs = advance_group(sm.page_prefix, gs, j);
       if (gs != cur_g) {
-        // new group: its rows, query fragments, head weights and outputs
-        // (waiting for these loads drains the page requests in flight;
-        // groups change only a few times per wave)
-        int L[RG], ql[RG];
-        bool rl[RG];
-        const GroupDesc gd = describe_group<RG>(R, sm.req_tab, gs, group_request<RG>(R, sm.req_tab, gs), L, ql, rl);
-        load_query<D, RG, MT>(p, ql, qf);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          float wv = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
-          if (!rl[r] || lane >= p.heads) wv = 0.0f;
-          wbuf[r][lane] = wv;
-          out[r] = row_out(p.logits + static_cast<int64_t>(gd.row0 + r) * p.logits_stride + gd.col0,
-                           r < gd.nrows ? L[r] : 0);
-        }
-        __builtin_amdgcn_wave_barrier();
-        const int hg = 4 * (lane >> 5);
-#pragma unroll
-        for (int r = 0; r < RG; ++r)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const float4 x = *reinterpret_cast<const float4*>(&wbuf[r][32 * mt + 8 * i4 + hg]);
-              wf.v[r][mt][4 * i4 + 0] = x.x;
-              wf.v[r][mt][4 * i4 + 1] = x.y;
-              wf.v[r][mt][4 * i4 + 2] = x.z;
-              wf.v[r][mt][4 * i4 + 3] = x.w;
-            }
+        // a later group (waiting for its loads drains the page requests in
+        // flight; a wave's range crosses few group boundaries)
+        setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out);
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
