@@ -44,6 +44,7 @@ constexpr int kD1Bins = 4096;
 constexpr int kD1Shift = 20;
 constexpr int kCandCap = 4096;
 constexpr int kBitmapWords = 4096;  // bitmap path for rows up to 131072 keys
+constexpr int kRankCap = 256;       // threshold-bin keys ranked pairwise
 constexpr int kRowCap = 32768;      // keys of an LDS-resident row
 
 template <int NT>
@@ -399,25 +400,41 @@ __device__ void select_row_stream(const float* __restrict__ row, int L, int k, i
 template <int NT, int E>
 __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int* __restrict__ out,
                                SelectShared<NT>& sm) {
-  constexpr int NW = NT / kWave;
+  static_assert(E % 4 == 0, "keys per thread come in quads");
+  constexpr int EQ = E / 4;  // quads per thread: quad q = tid + NT j holds keys 4q .. 4q + 3
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int nj = (L + NT - 1) / NT;  // register slots in use (uniform)
+  const int nq = ((L + 3) / 4 + NT - 1) / NT;  // quad slots in use (uniform)
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
 
-  // 1. load: all loads in flight at once
+  // 1. load (all loads in flight at once; 16-byte loads for whole quads of
+  //    an aligned row, clamped 4-byte loads otherwise) and the row's range
   float x[E];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int p = tid + NT * j;
-    if (j < nj) x[j] = row[p < L ? p : L - 1];
+  for (int j = 0; j < EQ; ++j) {
+    if (j < nq) {
+      const int p0 = 4 * (tid + NT * j);
+      if (aligned && p0 + 4 <= L) {
+        const float4 v = *reinterpret_cast<const float4*>(row + p0);
+        x[4 * j] = v.x;
+        x[4 * j + 1] = v.y;
+        x[4 * j + 2] = v.z;
+        x[4 * j + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = row[p0 + e < L ? p0 + e : L - 1];
+      }
+    }
   }
   float lo = __builtin_inff(), hi = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < nj) {
-      lo = fminf(lo, x[j]);
-      hi = fmaxf(hi, x[j]);
+  for (int j = 0; j < EQ; ++j) {
+    if (j < nq) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo = fminf(lo, x[4 * j + e]);
+        hi = fmaxf(hi, x[4 * j + e]);
+      }
     }
   }
   for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
@@ -431,109 +448,119 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
   float a = half_range > 0.0f ? static_cast<float>(kD1Bins / 2) / half_range : 0.0f;
   float b = -(lo * a);
   if (!(__builtin_fabsf(a) <= 3.0e38f) || !(__builtin_fabsf(b) <= 3.0e38f)) a = b = 0.0f;
-  auto bin_of = [&](float v) -> int {
-    return static_cast<int>(__builtin_amdgcn_fmed3f(__builtin_fmaf(v, a, b), 0.0f, static_cast<float>(kD1Bins - 1)));
-  };
 
-  // 2. first-digit histogram and the bin B1 holding the k-th largest
+  // 2. first-digit histogram (bins kept; -1 marks slots past L) and the bin
+  //    B1 holding the k-th largest
+  int bn[E];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < nj && tid + NT * j < L) atomicAdd(&sm.u.hist1[bin_of(x[j])], 1);
+  for (int j = 0; j < EQ; ++j) {
+    if (j < nq) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = 4 * (tid + NT * j) + e;
+        const int v = static_cast<int>(
+            __builtin_amdgcn_fmed3f(__builtin_fmaf(x[4 * j + e], a, b), 0.0f, static_cast<float>(kD1Bins - 1)));
+        bn[4 * j + e] = p < L ? v : -1;
+        if (p < L) atomicAdd(&sm.u.hist1[v], 1);
+      }
+    }
   }
   __syncthreads();
   int B1, above1, cnt1;
   find_digit<NT>(kD1Bins, k, [&](int d) { return sm.u.hist1[d]; }, sm, B1, above1, cnt1);
-  const int n_cand = above1 + cnt1;
-  if (n_cand > kCandCap) {
-    // too many keys at or above B1 (large ties): radix-select from global
+  if (cnt1 > kCandCap) {
+    // too many keys in the threshold bin (large ties): radix-select from
+    // global memory
     select_row_stream<NT>(row, L, k, out, sm);
     return;
   }
 
-  // 3. candidates (bin >= B1) -> (key, position) list: per-wave counts,
-  //    their prefix over the waves, then ordered writes within each wave
-  int c_own = 0;
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < nj) c_own += __popcll(__ballot(tid + NT * j < L && bin_of(x[j]) >= B1));
-  }
-  if (lane == 0) sm.scan[wave] = c_own;
+  // 3. winners above bin B1 straight into the position bitmap: the 4 keys
+  //    of a quad give a nibble, the 8 quads of a 32-position word sit in 8
+  //    consecutive lanes (q % 8 == lane % 8), and an OR over those lanes
+  //    gives the word, stored by its first lane.  Keys in bin B1 go to a
+  //    short list (positions only) for the exact decision.
+  uint32_t* bits = sm.u.sel;  // hist1 is dead once B1 is known
+  int* eq_pos = sm.c.cidx;
+  uint32_t* eq_key = sm.c.ckey;
+  if (tid == 0) sm.bc[4] = 0;
   __syncthreads();
-  int pos = 0;
-  for (int w = 0; w < wave; ++w) pos += sm.scan[w];
+  const int need = k - above1;  // keys of bin B1 to take
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < nj) {
-      const int p = tid + NT * j;
-      const int b = bin_of(x[j]);
-      const bool c = p < L && b >= B1;
-      const uint64_t m = __ballot(c);
-      if (c) {
-        const int slot = pos + mbcnt64(m);
-        // above-bin candidates carry key 0xFFFFFFFF: they always win
-        sm.c.ckey[slot] = b > B1 ? 0xFFFFFFFFu : ordered_key(x[j]);
-        sm.c.cidx[slot] = p;
+  for (int j = 0; j < EQ; ++j) {
+    if (j < nq) {
+      const int q = tid + NT * j;
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gt |= (bn[4 * j + e] > B1 ? 1u : 0u) << e;
+        eq |= (bn[4 * j + e] == B1 ? 1u : 0u) << e;
       }
-      pos += __popcll(m);
+      uint32_t w = gt << (4 * (lane & 7));
+      w |= __builtin_amdgcn_update_dpp(0u, w, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+      w |= __builtin_amdgcn_update_dpp(0u, w, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+      w |= __builtin_amdgcn_update_dpp(0u, w, 0x141, 0xF, 0xF, false);  // row_half_mirror
+      if ((lane & 7) == 0) bits[q >> 3] = w;
+      while (eq) {
+        const int e = __builtin_ctz(eq);
+        eq &= eq - 1u;
+        const int slot = atomicAdd(&sm.bc[4], 1);
+        if (slot < kCandCap) eq_pos[slot] = 4 * q + e;
+      }
     }
   }
   __syncthreads();
-  const int nc = n_cand;
+  const int m = cnt1;
 
-  // 4. exact threshold key among the candidates of bin B1 (need = k - above1)
-  SelectState st{0u, 0u, k - above1};
-  int n_eq = cnt1;
-  if (st.need != cnt1) {
-    auto in_bin = [&](auto fn) {
-      for (int i = tid; i < nc; i += NT) {
-        const uint32_t key = sm.c.ckey[i];
-        if (key != 0xFFFFFFFFu) fn(key);
+  // 4. the `need` winners of bin B1: largest exact key, ties to the lowest
+  //    position.  Few keys: rank each against all; more: radix passes.
+  for (int i = tid; i < m; i += NT) eq_key[i] = ordered_key(row[eq_pos[i]]);
+  __syncthreads();
+  if (need == m) {
+    for (int i = tid; i < m; i += NT) atomicOr(&bits[eq_pos[i] >> 5], 1u << (eq_pos[i] & 31));
+  } else if (m <= kRankCap) {
+    for (int i = tid; i < m; i += NT) {
+      const uint32_t ki = eq_key[i];
+      const int pi = eq_pos[i];
+      int rank = 0;
+      for (int u = 0; u < m; ++u) {
+        const uint32_t ku = eq_key[u];
+        rank += (ku > ki || (ku == ki && eq_pos[u] < pi)) ? 1 : 0;
       }
+      if (rank < need) atomicOr(&bits[pi >> 5], 1u << (pi & 31));
+    }
+  } else {
+    SelectState st{0u, 0u, need};
+    auto in_bin = [&](auto fn) {
+      for (int i = tid; i < m; i += NT) fn(eq_key[i]);
     };
-    n_eq = refine_pass<NT>(st, 21, 11, in_bin, sm);
+    int n_eq = refine_pass<NT>(st, 21, 11, in_bin, sm);
     if (st.need != n_eq) n_eq = refine_pass<NT>(st, 10, 11, in_bin, sm);
     if (st.need != n_eq) n_eq = refine_pass<NT>(st, 0, 10, in_bin, sm);
-  } else {
-    st.pmask = 0u;  // bin B1 taken whole: every candidate wins
-    n_eq = nc;
-    st.need = nc;
-  }
-  // winners: key 0xFFFFFFFF (above B1), in-bin keys with (key & pmask) >
-  // prefix, and of those equal under pmask the `need` lowest positions
-
-  // 5. winners -> position bitmap
-  uint32_t* bits = sm.u.sel;
-  const int W = (L + 31) >> 5;
-  for (int j = tid; j < W; j += NT) bits[j] = 0u;
-  __syncthreads();
-  const bool take_all_eq = st.need == n_eq;
-  const uint32_t prefix = st.prefix, pmask = st.pmask;
-  for (int i = tid; i < nc; i += NT) {
-    const uint32_t key = sm.c.ckey[i];
-    const int p = sm.c.cidx[i];
-    const uint32_t m = key & pmask;
-    const bool above = key == 0xFFFFFFFFu && pmask != 0u;
-    if (above || m > prefix || (take_all_eq && m == prefix)) atomicOr(&bits[p >> 5], 1u << (p & 31));
-  }
-  if (!take_all_eq) {
-    // equal keys at the threshold: the `need` lowest positions among them,
-    // i.e. the largest of (2^17 - 1 - position), by radix select on 17 bits
-    SelectState ts{0u, 0u, st.need};
-    auto tied = [&](auto fn) {
-      for (int i = tid; i < nc; i += NT) {
-        const uint32_t key = sm.c.ckey[i];
-        if (key != 0xFFFFFFFFu && (key & pmask) == prefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.c.cidx[i]));
+    const bool take_all_eq = st.need == n_eq;
+    const uint32_t prefix = st.prefix, pmask = st.pmask;
+    for (int i = tid; i < m; i += NT) {
+      const uint32_t mk = eq_key[i] & pmask;
+      if (mk > prefix || (take_all_eq && mk == prefix)) atomicOr(&bits[eq_pos[i] >> 5], 1u << (eq_pos[i] & 31));
+    }
+    if (!take_all_eq) {
+      // keys equal to the threshold: the `need` lowest positions among them,
+      // i.e. the largest of (2^17 - 1 - position), by radix select on 17 bits
+      SelectState ts{0u, 0u, st.need};
+      auto tied = [&](auto fn) {
+        for (int i = tid; i < m; i += NT)
+          if ((eq_key[i] & pmask) == prefix) fn(0x1FFFFu - static_cast<uint32_t>(eq_pos[i]));
+      };
+      refine<NT>(ts, 8, 9, 0, 8, tied, sm);
+      for (int i = tid; i < m; i += NT) {
+        const int pi = eq_pos[i];
+        if ((eq_key[i] & pmask) == prefix && (0x1FFFFu - static_cast<uint32_t>(pi)) >= ts.prefix)
+          atomicOr(&bits[pi >> 5], 1u << (pi & 31));
       }
-    };
-    refine<NT>(ts, 8, 9, 0, 8, tied, sm);
-    for (int i = tid; i < nc; i += NT) {
-      const uint32_t key = sm.c.ckey[i];
-      const int p = sm.c.cidx[i];
-      if (key != 0xFFFFFFFFu && (key & pmask) == prefix && (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix)
-        atomicOr(&bits[p >> 5], 1u << (p & 31));
     }
   }
   __syncthreads();
+  const int W = (L + 31) >> 5;
 
   // 6. ordered emission: thread t owns bitmap words [t wpt, (t + 1) wpt)
   const int wpt = (W + NT - 1) / NT;
@@ -552,7 +579,6 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
     }
   }
   __syncthreads();
-  (void)NW;
 }
 
 // Top-k of one row.

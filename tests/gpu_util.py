@@ -75,6 +75,11 @@ class Dev:
         return out.cpu().numpy(), ws
 
 
+def topk_workspace(rows, k, device="cuda"):
+    """A zeroed workspace sized for idx_topk on these rows."""
+    return idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_TOPK, None, rows, 0, k), device)
+
+
 def check_logits(got_rows: np.ndarray, ref: dict, col0=None, check_untouched=True, label=""):
     """got_rows[r] is the GPU logits row; ref[r] the oracle's [L] logits."""
     for r, lg in ref.items():

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import sparse_attention_indexer_decode_amd as idx
-from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows
+from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows, topk_workspace
 from workloads import config
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,8 @@ def test_decode_config_every_row(name):
     R = len(L)
     buf = fp32_rows(ref, R, got.shape[1])
     o2 = torch.full((R, wl.topk), -7, dtype=torch.int32, device=dev.device)
-    idx.idx_topk(torch.from_numpy(buf).to(dev.device), dev.decode_rows(), wl.topk, o2, idx.new_workspace(256))
+    idx.idx_topk(torch.from_numpy(buf).to(dev.device), dev.decode_rows(), wl.topk, o2,
+                 topk_workspace(dev.decode_rows(), wl.topk))
     o2 = o2.cpu().numpy()
     for r in range(R):
         exp = oracle.topk.topk_row(buf[r, : L[r]].astype(np.float64), int(L[r]), wl.topk)
@@ -109,7 +110,7 @@ def test_prefill_c5_chunks_sampled():
         M, N = rec["q_end"] - rec["q_begin"], rec["total_seq_lens"]
         q, w = dev.chunk_queries(rec)
         logits = torch.empty((M, N), device=dev.device)
-        ws = idx.new_workspace(256)
+        ws = topk_workspace(rows, wl.topk)
         idx.idx_logits_paged(dev.cache, rows, q, w, logits, ws)
         out = torch.full((M, wl.topk), -7, dtype=torch.int32, device=dev.device)
         idx.idx_topk(logits, rows, wl.topk, out, ws)

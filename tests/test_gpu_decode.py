@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import sparse_attention_indexer_decode_amd as idx
-from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows
+from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows, topk_workspace
 from workloads import build_decode, config
 
 pytestmark = pytest.mark.gpu
@@ -117,7 +117,7 @@ def test_topk_bitexact_on_given_logits(k):
     rows_d = idx.Rows.decode(bt, seq, max(lens))
     logits = torch.from_numpy(buf).to(d)
     out = torch.full((R, k), -7, dtype=torch.int32, device=d)
-    ws = idx.new_workspace(256, d)
+    ws = topk_workspace(rows_d, k, d)
     idx.idx_topk(logits, rows_d, k, out, ws)
     got = out.cpu().numpy()
     for r, v in enumerate(rows):
@@ -135,7 +135,8 @@ def test_topk_bitexact_on_oracle_logits():
     d = torch.device("cuda")
     dev = Dev(wl)
     out = torch.full((R, wl.topk), -7, dtype=torch.int32, device=d)
-    idx.idx_topk(torch.from_numpy(buf).to(d), dev.decode_rows(), wl.topk, out, idx.new_workspace(256, d))
+    idx.idx_topk(torch.from_numpy(buf).to(d), dev.decode_rows(), wl.topk, out,
+                 topk_workspace(dev.decode_rows(), wl.topk, d))
     got = out.cpu().numpy()
     for r in range(R):
         exp = oracle.topk.topk_row(buf[r, : L[r]].astype(np.float64), int(L[r]), wl.topk)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import sparse_attention_indexer_decode_amd as idx
-from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows
+from tests.gpu_util import Dev, check_logits, check_topk_e2e, fp32_rows, topk_workspace
 from workloads import build_prefill
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,7 @@ def _run_chunk(dev, rec):
     ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_LOGITS, dev.cache, rows, wl.heads, 0), dev.device)
     idx.idx_logits_paged(dev.cache, rows, q, w, logits, ws)
     out = torch.full((M, wl.topk), -7, dtype=torch.int32, device=dev.device)
-    idx.idx_topk(logits, rows, wl.topk, out, idx.new_workspace(256, dev.device))
+    idx.idx_topk(logits, rows, wl.topk, out, topk_workspace(rows, wl.topk, dev.device))
     torch.cuda.synchronize()
     assert idx.idx_read_device_status(ws) == 0
     return logits.cpu().numpy(), out.cpu().numpy(), rows
@@ -65,7 +65,7 @@ def test_prefill_chunks_logits_and_topk(case):
         # and bit-exact on the oracle's fp32 logits
         buf = fp32_rows(ref, got.shape[0], got.shape[1], col0=ks)
         o2 = torch.full((got.shape[0], k), -7, dtype=torch.int32, device=dev.device)
-        idx.idx_topk(torch.from_numpy(buf).to(dev.device), rows, k, o2, idx.new_workspace(256, dev.device))
+        idx.idx_topk(torch.from_numpy(buf).to(dev.device), rows, k, o2, topk_workspace(rows, k, dev.device))
         o2 = o2.cpu().numpy()
         for r in range(got.shape[0]):
             exp = oracle.topk.topk_row(buf[r, ks[r] : ks[r] + L[r]].astype(np.float64), int(L[r]), k)
