@@ -13,8 +13,9 @@ Timing: inputs are resident in HBM before the timed region.  The pool
 (169 MB) would fit the 256 MiB MALL, so each step reads one of `--copies`
 identical pools in rotation (8 x 169 MB by default); between two uses of a
 pool ~550 MB of other keys stream through, so the keys come from HBM.  K
-steps are bracketed by synchronisation; HIP events on the launch stream
-give the per-launch duration used for the roofline.
+steps are bracketed by synchronisation (the value); the same K steps are
+then run with HIP events on the launch stream around each launch, which give
+the per-launch durations used for the roofline.
 
 Prints one JSON line.  `--summarize-prof DIR...` turns rocprofv3 outputs
 (kernel-trace stats and FETCH_SIZE / WRITE_SIZE counter runs) into
@@ -181,13 +182,22 @@ def run(args):
     torch.cuda.synchronize()
     assert torch.equal(first, fused), "idx_decode_topk differs from idx_logits_paged + idx_topk"
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K whole steps back to back (wall clock between syncs)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    assert torch.equal(first, outs), "decode top-k is not deterministic across steps"
+    # the same K steps again with HIP events on the launch stream around each
+    # of the two launches (per-kernel durations for the roofline; the events
+    # themselves cost a few us per step, so the value above is taken without)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
     score_ms = [e[0].elapsed_time(e[1]) for e in evs]
     topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
     assert torch.equal(first, outs), "decode top-k is not deterministic across steps"
