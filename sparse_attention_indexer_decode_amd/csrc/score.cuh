@@ -428,8 +428,8 @@ __device__ __forceinline__ int group_of_page(const int* page_prefix, int ng, int
   return lo;
 }
 
-// Physical ids of global pages jb + lane (one per lane, page 0 past j1).  Ids
-// outside the pool set the status flag and read page 0 instead.
+// Block-table entries of global pages jb + lane (one per lane, 0 past j1);
+// checked against the pool where they are used.
 template <int RG>
 __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_prefix,
                                         const int (*req_tab)[kMaxReqPrefill + 1], int ng, int jb, int j1) {
@@ -438,10 +438,7 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
   const RowArgs& R = p.rows;
   const int g = group_of_page(page_prefix, ng, j);
   const int b = group_request<RG>(R, req_tab, g);
-  const int id = R.block_table[static_cast<int64_t>(b) * R.bt_stride + (j - page_prefix[g])];
-  const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
-  if (!ok) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, 1u);
-  return ok ? id : 0;
+  return R.block_table[static_cast<int64_t>(b) * R.bt_stride + (j - page_prefix[g])];
 }
 
 // A group's rows, query fragments, head weights (through the wave's LDS
@@ -524,6 +521,7 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
   float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
   const uint32_t buf_lds[2] = {lds_addr(sm.page[wave][0]), lds_addr(sm.page[wave][1])};
 
+  bool bad_page = false;
   if (j0 < j1) {
     // Page ids come in batches of 64 (lane i: page jb + i), so that no
     // compiler-visible load sits between page requests; a later batch costs
@@ -535,7 +533,10 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
         jb = j;
         ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
       }
-      return __builtin_amdgcn_readlane(ids, j - jb);
+      const int id = __builtin_amdgcn_readlane(ids, j - jb);
+      const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
+      bad_page |= !ok;  // ids outside the pool read page 0 and are reported
+      return ok ? id : 0;
     };
 
     // The first group's queries and weights are loaded together with the
@@ -576,6 +577,7 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
     }
   }
   wait_all_loads();  // no request may still be writing LDS when the wave ends
+  if (bad_page && lane == 0) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, kStatusBadPage);
 }
 
 }  // namespace idx
