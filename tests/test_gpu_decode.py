@@ -169,3 +169,42 @@ def test_bad_page_id_flags_and_never_faults():
     _, ws = dev.logits_decode()
     assert idx.idx_read_device_status(ws) & idx.IDX_DEV_BAD_PAGE
     assert idx.idx_read_device_status(ws) == 0      # read clears it
+
+
+def test_decode_topk_in_a_hip_graph_replays():
+    """idx_decode_topk captured in a HIP graph: every replay, with other
+    eager work and synchronisation in between and new query contents each
+    time, gives the eager result for those contents."""
+    wl = _case("fp8", 128, 64, 2, False, seed=12)
+    dev = Dev(wl)
+    rows = dev.decode_rows()
+    k = wl.topk
+    d = dev.device
+    q_a = dev.q.clone()
+    q_b = torch.roll(dev.q, shifts=1, dims=0).contiguous()   # other rows' queries
+    qbuf = dev.q.clone()
+    out = torch.full((rows.num_rows, k), -7, dtype=torch.int32, device=d)
+    ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, dev.cache, rows, wl.heads, k), d)
+    refs = []
+    for qv in (q_a, q_b):
+        qbuf.copy_(qv)
+        idx.idx_decode_topk(dev.cache, rows, qbuf, dev.w, k, out, ws)
+        torch.cuda.synchronize()
+        refs.append(out.clone())
+    assert not torch.equal(refs[0], refs[1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        idx.idx_decode_topk(dev.cache, rows, qbuf, dev.w, k, out, ws)
+    torch.cuda.synchronize()
+    other = torch.full((rows.num_rows, max(dev.max_len, 1)), float("nan"), device=d)
+    ows = idx.new_workspace(256, d)
+    for i in range(6):
+        qbuf.copy_(q_a if i % 2 == 0 else q_b)
+        out.fill_(-7)
+        idx.idx_logits_paged(dev.cache, rows, dev.q, dev.w, other, ows)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[i % 2]), f"replay {i}"
