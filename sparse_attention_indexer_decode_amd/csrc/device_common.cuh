@@ -59,6 +59,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_all_loads() { wait_vmcnt<0>(); }
 
+// s_waitcnt lgkmcnt(0): every LDS (and scalar memory) access of the wave has
+// completed, e.g. before a direct load overwrites LDS the wave was reading.
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
 // Order-preserving map from float to uint32: larger float -> larger key.
 // -0.0 is first folded onto +0.0 so that both compare equal.
 __device__ __forceinline__ uint32_t ordered_key(float x) {

@@ -74,13 +74,26 @@ struct Geometry {
   static_assert(kLoads <= 15, "loads per page must fit a vmcnt immediate");
 };
 
-template <int D, bool MX, int RG, int NWV>
+// Bytes of a group's query block staged in LDS (full 32-head tiles of
+// 128 dims only; see load_query_staged).
+template <int D, int RG, int MT>
+constexpr int query_stage_bytes() { return D == 128 ? RG * MT * 32 * D * 2 : 0; }
+
+// Each wave's LDS area: its two-page ring, which also stages the first
+// group's queries before the first page is requested.
+template <int D, bool MX, int RG, int MT>
+union WaveArea {
+  uint8_t page[2][Geometry<D, MX>::kPageBytes];
+  uint8_t stage[query_stage_bytes<D, RG, MT>() > 0 ? query_stage_bytes<D, RG, MT>() : 16];
+};
+
+template <int D, bool MX, int RG, int MT, int NWV>
 struct ScoreShared {
   int page_prefix[kMaxGroups + 1];     // pages before each group
   int req_tab[4][kMaxReqPrefill + 1];  // prefill: groups, rows, columns, first query; decode: packed offsets
   float wbuf[NWV][RG][kMaxHeads];
   int misc[16];
-  uint8_t page[NWV][2][Geometry<D, MX>::kPageBytes];
+  alignas(16) WaveArea<D, MX, RG, MT> area[NWV];
 };
 
 struct GroupDesc {
@@ -250,6 +263,49 @@ __device__ __forceinline__ void load_query(const ScoreParams& p, const int (&qlo
       for (int s = 0; s < D / 16; ++s) f.a[r][mt][s] = __builtin_bit_cast(v8bf, src[s]);
     }
   }
+}
+
+// The same fragments for D = 128 and heads = 32 MT, read through the wave's
+// idle LDS area.  Loaded directly, each 16-byte fragment load of a wave
+// touches 64 different 128-byte lines (32 heads x 2 lane halves); here every
+// load instruction reads 1 KiB of contiguous query (4 heads), the 16-byte
+// chunks are written to LDS, and the fragments are read back.  Chunk c of
+// head h (dims 8c .. 8c + 7, within row r's block) sits at 16-byte slot
+// 16 h + (c ^ (h % 16) ^ ((h / 16) % 2)): the XOR keeps the 16 (or 32)
+// lanes of each b128 access on distinct bank groups, for the writes (one
+// head per 16 lanes) and the fragment reads (one head per lane) alike.
+// The caller must not reuse the area before the reads have returned.
+template <int D, int RG, int MT>
+__device__ __forceinline__ void load_query_staged(const ScoreParams& p, const int (&qload)[RG], uint8_t* area,
+                                                  QFrag<D, RG, MT>& f) {
+  static_assert(D == 128, "staging assumes 16 chunks of 16 bytes per head");
+  constexpr int kHeads = 32 * MT;
+  constexpr int kLoads = kHeads * D * 2 / 1024;  // 1 KiB per load instruction
+  const int lane = lane_id();
+  auto slot = [](int h, int c) { return 16 * h + (c ^ (h & 15) ^ ((h >> 4) & 1)); };
+  u32x4 v[RG][kLoads];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + static_cast<int64_t>(qload[r] >= 0 ? qload[r] : 0) * kHeads * D);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) v[r][i] = src[64 * i + lane];
+  }
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_u32x4* st = (lds_u32x4*)area;  // LDS accesses, whatever the compiler infers
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) st[r * kHeads * 16 + slot(4 * i + lane / 16, lane % 16)] = v[r][i];
+  __builtin_amdgcn_wave_barrier();
+  const int m = lane & 31;
+  const int g = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        f.a[r][mt][s] = __builtin_bit_cast(v8bf, st[r * kHeads * 16 + slot(32 * mt + m, 8 * g + s)]);
 }
 
 // max(x, 0) in one instruction: as signed integers, negative floats
@@ -443,16 +499,22 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
 
 // A group's rows, query fragments, head weights (through the wave's LDS
 // staging row, into the accumulator layout) and output descriptors.
+// `stage` is the wave's idle LDS area for a staged query load, or null.
 template <int D, int RG, int MT>
 __device__ __forceinline__ void setup_group(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
                                             float (*wbuf)[kMaxHeads], QFrag<D, RG, MT>& qf, WFrag<RG, MT>& wf,
-                                            RowOut (&out)[RG]) {
+                                            RowOut (&out)[RG], uint8_t* stage) {
   const RowArgs& R = p.rows;
   const int lane = lane_id();
   int L[RG], ql[RG];
   bool rl[RG];
   const GroupDesc gd = describe_group<RG>(R, req_tab, g, group_request<RG>(R, req_tab, g), L, ql, rl);
-  load_query<D, RG, MT>(p, ql, qf);
+  if constexpr (query_stage_bytes<D, RG, MT>() > 0) {
+    if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, RG, MT>(p, ql, stage, qf);
+    else load_query<D, RG, MT>(p, ql, qf);
+  } else {
+    load_query<D, RG, MT>(p, ql, qf);
+  }
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     float wv = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
@@ -482,7 +544,7 @@ template <int D, bool MX, int RG, int MT>
 __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(ScoreParams p) {
   constexpr int kScoreWaves = score_waves(RG, MT);
   constexpr int kScoreThreads = kScoreWaves * kWave;
-  __shared__ ScoreShared<D, MX, RG, kScoreWaves> sm;
+  __shared__ ScoreShared<D, MX, RG, MT, kScoreWaves> sm;
   const RowArgs& R = p.rows;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -519,7 +581,8 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
   const int j1 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * (W + 1) / NW));
 
   float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
-  const uint32_t buf_lds[2] = {lds_addr(sm.page[wave][0]), lds_addr(sm.page[wave][1])};
+  WaveArea<D, MX, RG, MT>& area = sm.area[wave];
+  const uint32_t buf_lds[2] = {lds_addr(area.page[0]), lds_addr(area.page[1])};
 
   bool bad_page = false;
   if (j0 < j1) {
@@ -547,13 +610,14 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
     RowOut out[RG];
     int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
     int g_first = 0;                                  // its first global page
-    setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out);
+    setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out, area.stage);
     g_first = sm.page_prefix[gs];
     int cur_g = gs;
 
     const int id0 = id_of(j0);
     const int id1 = j0 + 1 < j1 ? id_of(j0 + 1) : 0;
     wait_all_loads();  // nothing the compiler loaded before is still in flight
+    wait_lds();        // the staged query reads have returned: the area is free
     dma_page<D, MX>(p, id0, buf_lds[0]);
     if (j0 + 1 < j1) dma_page<D, MX>(p, id1, buf_lds[1]);
 
@@ -562,7 +626,7 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       if (gs != cur_g) {
         // a later group (waiting for its loads drains the page requests in
         // flight; a wave's range crosses few group boundaries)
-        setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out);
+        setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out, nullptr);
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
@@ -572,7 +636,7 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       if (j + 1 < j1) wait_all_but_last_page<D, MX>();
       else wait_all_loads();
       const int slot = (j - j0) & 1;
-      score_page<D, MX, RG, MT>(sm.page[wave][slot], wf, qf, out, j - g_first);
+      score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
       if (j + 2 < j1) dma_page<D, MX>(p, nxt, buf_lds[slot]);  // page j + 2 into the freed buffer
     }
   }
