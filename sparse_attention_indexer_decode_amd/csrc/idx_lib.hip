@@ -112,7 +112,10 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   return IDX_OK;
 }
 
-int pick_rg(const RowArgs& R) { return (R.kind == 0 && R.next_n == 1) ? 1 : 2; }
+int pick_rg(const RowArgs& R) {
+  if (R.kind != 0) return kBlockRows;  // prefill: one group of consecutive rows per workgroup
+  return R.next_n == 1 ? 1 : 2;
+}
 
 // Upper bound of the scorer's row groups.
 int64_t group_bound(const RowArgs& R, int rg) {
@@ -139,10 +142,26 @@ hipError_t launch_score(const ScoreParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool MX, int MT>
+hipError_t launch_block(const ScoreParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((score_block_kernel<D, MX, MT>), dim3(grid), dim3(kBlockRows * kWave), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s) {
   const int d = p.cache.head_dim;
   const bool mx = p.cache.fmt == IDX_FMT_MXFP4;
   const int mt = p.heads > 32 ? 2 : 1;
+  if (p.rows.kind != 0) {
+#define IDX_BLOCK_CASE(D_, MX_, MT_) \
+  if (d == D_ && mx == MX_ && mt == MT_) return launch_block<D_, MX_, MT_>(p, grid, s);
+    IDX_BLOCK_CASE(128, false, 1) IDX_BLOCK_CASE(128, false, 2)
+    IDX_BLOCK_CASE(64, false, 1) IDX_BLOCK_CASE(64, false, 2)
+    IDX_BLOCK_CASE(32, false, 1) IDX_BLOCK_CASE(32, false, 2)
+    IDX_BLOCK_CASE(128, true, 1) IDX_BLOCK_CASE(128, true, 2)
+#undef IDX_BLOCK_CASE
+    return hipErrorInvalidValue;
+  }
 #define IDX_SCORE_CASE(D_, MX_, RG_, MT_) \
   if (d == D_ && mx == MX_ && rg == RG_ && mt == MT_) return launch_score<D_, MX_, RG_, MT_>(p, grid, s);
 #define IDX_SCORE_RGMT(D_, MX_) \

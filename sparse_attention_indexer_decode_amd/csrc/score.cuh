@@ -322,36 +322,36 @@ __device__ __forceinline__ float ue8m0_to_float(uint32_t e) {
   return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23));
 }
 
+// K-step s of one key's B fragment (this lane's 8 dims of the step) decoded
+// to bf16: fp8 codes exactly, or e2m1 values times their MX block scale.
+template <int D, bool MX>
+__device__ __forceinline__ v8bf key_step(const uint8_t* rowp, int g, int s) {
+  if (MX) {
+    // D = 128: packed bytes [32 g, 32 g + 32) = blocks 2g, 2g+1 (dims 64 g ..)
+    const uint32_t x = reinterpret_cast<const uint32_t*>(rowp + 32 * g)[s];
+    const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rowp + D / 2 + 2 * g);
+    const float f = ue8m0_to_float(s < 4 ? (sc2 & 0xFFu) : (sc2 >> 8));
+    const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 3))};
+    return __builtin_bit_cast(v8bf, r);
+  } else {
+    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rowp + g * (D / 2));
+    const uint32_t x0 = w32[2 * s], x1 = w32[2 * s + 1];
+    const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true))};
+    return __builtin_bit_cast(v8bf, r);
+  }
+}
+
 // B fragments of one key (this lane's half of its dims) decoded to bf16.
 template <int D, bool MX>
 __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (&b)[D / 16]) {
-  if (MX) {
-    // D = 128: packed bytes [32 g, 32 g + 32) = blocks 2g, 2g+1 (dims 64 g ..)
-    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rowp + 32 * g);
-    const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rowp + D / 2 + 2 * g);
-    const float sc[2] = {ue8m0_to_float(sc2 & 0xFFu), ue8m0_to_float(sc2 >> 8)};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const uint32_t x = w32[s];
-      const float f = sc[s / 4];
-      const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 0)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 1)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 2)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 3))};
-      b[s] = __builtin_bit_cast(v8bf, r);
-    }
-  } else {
-    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rowp + g * (D / 2));
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const uint32_t x0 = w32[2 * s], x1 = w32[2 * s + 1];
-      const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false)),
-                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true))};
-      b[s] = __builtin_bit_cast(v8bf, r);
-    }
-  }
+  for (int s = 0; s < D / 16; ++s) b[s] = key_step<D, MX>(rowp, g, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,13 +421,12 @@ __device__ __forceinline__ void finish_key(const float (&ps)[4], float key_scale
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out, off, 0, 0);
 }
 
-// Scores the 64 keys of the page in LDS for every row of the group and
-// stores logit t = 64 pg + key of each.  The MFMAs of the second 32-key tile
-// are issued before the head sums of the first, so that those VALU sums run
-// while the matrix core works.
+// Raw scores of one row against the 64 keys of the page in LDS: for each
+// 32-key tile nt, the MT accumulator tiles (heads x keys) and the keys' fp8
+// scales.
 template <int D, bool MX, int RG, int MT>
-__device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, MT>& wf, const QFrag<D, RG, MT>& qf,
-                                           const RowOut (&out)[RG], int pg) {
+__device__ __forceinline__ void page_mfma(const uint8_t* buf, const QFrag<D, RG, MT>& qf, int r, v16f (&acc)[2][MT],
+                                          float (&key_scale)[2]) {
   using Geo = Geometry<D, MX>;
   constexpr int KS = Geo::kKSteps;
   constexpr int RB = Geo::kRowBytes;
@@ -435,36 +434,80 @@ __device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, M
   const int n = lane & 31;
   const int g = lane >> 5;
 #pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint8_t* rowp = buf + (nt * 32 + n) * RB;
+    v8bf bfr[KS];
+    key_fragments<D, MX>(rowp, g, bfr);
+    key_scale[nt] = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v16f{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc[nt][mt], 0, 0, 0);
+  }
+}
+
+// Logits of page pg of one row from its raw scores: weighted ReLU head sums,
+// stored at t = 64 pg + key.
+template <int RG, int MT>
+__device__ __forceinline__ void page_logits(const v16f (&acc)[2][MT], const float (&key_scale)[2],
+                                            const WFrag<RG, MT>& wf, int r, const RowOut& out, int pg) {
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int g = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) head_sum<RG, MT>(acc[nt][mt], wf, r, mt, ps);
+    finish_key(ps, key_scale[nt], out, g == 0 ? (pg * kPage + nt * 32 + n) * 4 : 0x7FFFFFF0);
+  }
+}
+
+// Scores the 64 keys of the page in LDS for every row of the group and
+// stores logit t = 64 pg + key of each.  The MFMAs of the second 32-key tile
+// are issued before the head sums of the first, so that those VALU sums run
+// while the matrix core works.
+template <int D, bool MX, int RG, int MT>
+__device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, MT>& wf, const QFrag<D, RG, MT>& qf,
+                                           const RowOut (&out)[RG], int pg) {
+#pragma unroll
   for (int r = 0; r < RG; ++r) {
     v16f acc[2][MT];
     float key_scale[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint8_t* rowp = buf + (nt * 32 + n) * RB;
-      v8bf bfr[KS];
-      key_fragments<D, MX>(rowp, g, bfr);
-      key_scale[nt] = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v16f{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc[nt][mt], 0, 0, 0);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) head_sum<RG, MT>(acc[nt][mt], wf, r, mt, ps);
-      finish_key(ps, key_scale[nt], out[r], g == 0 ? (pg * kPage + nt * 32 + n) * 4 : 0x7FFFFFF0);
-    }
+    page_mfma<D, MX, RG, MT>(buf, qf, r, acc, key_scale);
+    page_logits<RG, MT>(acc, key_scale, wf, r, out[r], pg);
   }
 }
 
 // ---------------------------------------------------------------------------
 // The scorer kernel
 // ---------------------------------------------------------------------------
+
+// Pages per group -> exclusive prefix in sm.page_prefix[0 .. NG] (LDS).
+template <int RG, int NT, class SM>
+__device__ __forceinline__ void build_page_prefix(const RowArgs& R, SM& sm, int NG) {
+  const int tid = threadIdx.x;
+  int run = 0;
+  for (int base = 0; base < NG; base += NT) {
+    const int g = base + tid;
+    int np = 0;
+    if (g < NG) {
+      int L[RG], ql[RG];
+      bool rl[RG];
+      const GroupDesc d = describe_group<RG>(R, sm.req_tab, g, group_request<RG>(R, sm.req_tab, g), L, ql, rl);
+      np = (d.Lmax + kPage - 1) / kPage;
+    }
+    int tot;
+    const int ex = block_exclusive_scan<NT>(np, tot, sm.misc);
+    if (g < NG) sm.page_prefix[g] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) sm.page_prefix[NG] = run;
+  __syncthreads();
+}
 
 // Page j of the global list -> (group, page within group) by walking the
 // prefix from the previous group (pages of a wave are visited in order).
@@ -552,26 +595,7 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
   const bool tables = R.kind != 0 || R.q_packed;
   const int NG = tables ? build_request_tables<RG, kScoreThreads>(R, sm) : p.num_groups;
 
-  // pages per group -> prefix in LDS
-  {
-    int run = 0;
-    for (int base = 0; base < NG; base += kScoreThreads) {
-      const int g = base + tid;
-      int np = 0;
-      if (g < NG) {
-        int L[RG], ql[RG];
-        bool rl[RG];
-        const GroupDesc d = describe_group<RG>(R, sm.req_tab, g, group_request<RG>(R, sm.req_tab, g), L, ql, rl);
-        np = (d.Lmax + kPage - 1) / kPage;
-      }
-      int tot;
-      const int ex = block_exclusive_scan<kScoreThreads>(np, tot, sm.misc);
-      if (g < NG) sm.page_prefix[g] = run + ex;
-      run += tot;
-    }
-    if (tid == 0) sm.page_prefix[NG] = run;
-    __syncthreads();
-  }
+  build_page_prefix<RG, kScoreThreads>(R, sm, NG);
   const int P = sm.page_prefix[NG];
 
   // this wave's contiguous page range
@@ -639,6 +663,224 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
       if (j + 2 < j1) dma_page<D, MX>(p, nxt, buf_lds[slot]);  // page j + 2 into the freed buffer
     }
+  }
+  wait_all_loads();  // no request may still be writing LDS when the wave ends
+  if (bad_page && lane == 0) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, kStatusBadPage);
+}
+
+// ---------------------------------------------------------------------------
+// The prefill scorer: one page ring per workgroup
+// ---------------------------------------------------------------------------
+//
+// Prefill rows come in long runs of one request whose key ranges differ by
+// one key per row, so here a group is kBlockRows consecutive query rows and
+// each wave scores one of them: every page is read from memory once per
+// group and shared by the eight waves through a ring of kRing page buffers
+// in LDS.  Wave 0 requests pages kRing - 1 ahead.  Each page is decoded to
+// bf16 once, by all waves together (an eighth each), into one of two
+// decoded-page buffers, so that the per-row VALU work is the head sums.
+
+// Logits of one 32-key tile from its raw scores; `off` is the byte offset
+// of this lane's key in the row (out of range: nothing stored).
+template <int MT>
+__device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_scale, const WFrag<1, MT>& wf,
+                                            const RowOut& out, int off) {
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) head_sum<1, MT>(acc[mt], wf, 0, mt, ps);
+  finish_key(ps, key_scale, out, (lane_id() >> 5) == 0 ? off : 0x7FFFFFF0);
+}
+
+constexpr int kBlockRows = 8;  // rows per group = waves per workgroup
+constexpr int kRing = 4;       // page buffers per workgroup
+
+template <int D, bool MX>
+struct BlockShared {
+  int page_prefix[kMaxGroups + 1];
+  int req_tab[4][kMaxReqPrefill + 1];
+  float wbuf[kBlockRows][1][kMaxHeads];
+  int misc[16];
+  alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
+  alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
+};
+
+// Decodes this wave's share of a raw page into B-fragment order: fragment
+// (tile nt, k-step s) of lane l goes to dec[(nt KS + s) 64 + l], so that a
+// wave reads a fragment with one contiguous 1 KiB LDS access.  The 2 KS
+// fragment blocks of a page are spread over the waves.
+template <int D, bool MX>
+__device__ __forceinline__ void decode_page_slice(const uint8_t* raw, v8bf* dec, int wave) {
+  constexpr int KS = D / 16;
+  const int lane = lane_id();
+#pragma unroll
+  for (int b0 = 0; b0 < 2 * KS; b0 += kBlockRows) {
+    const int blk = b0 + wave;
+    if (blk < 2 * KS) {
+      const int nt = blk / KS, s = blk % KS;
+      dec[blk * kWave + lane] = key_step<D, MX>(raw + (nt * 32 + (lane & 31)) * Geometry<D, MX>::kRowBytes, lane >> 5, s);
+    }
+  }
+}
+
+// Raw scores of one row against 32-key tile nt of a decoded page (fp8 token
+// scales from the raw page).
+template <int D, bool MX, int MT>
+__device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, int nt, const QFrag<D, 1, MT>& qf,
+                                          v16f (&acc)[MT], float& key_scale) {
+  constexpr int KS = D / 16;
+  const int lane = lane_id();
+  key_scale = MX ? 1.0f : *reinterpret_cast<const float*>(raw + (nt * 32 + (lane & 31)) * Geometry<D, MX>::kRowBytes + D);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v16f{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const v8bf b = dec[(nt * KS + s) * kWave + lane];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[0][mt][s], b, acc[mt], 0, 0, 0);
+  }
+}
+
+// This wave's row (row `wave` of group g): query fragments, weights and
+// output descriptor.
+template <int D, int MT>
+__device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
+                                                int wave, float (*wbuf)[kMaxHeads], QFrag<D, 1, MT>& qf,
+                                                WFrag<1, MT>& wf, RowOut (&out)[1]) {
+  const RowArgs& R = p.rows;
+  const int lane = lane_id();
+  int L[kBlockRows], ql[kBlockRows];
+  bool rl[kBlockRows];
+  const GroupDesc gd =
+      describe_group<kBlockRows>(R, req_tab, g, group_request<kBlockRows>(R, req_tab, g), L, ql, rl);
+  const bool exists = wave < gd.nrows;
+  const int qrow[1] = {exists ? ql[wave] : -1};
+  load_query<D, 1, MT>(p, qrow, qf);
+  float wv = p.w[static_cast<int64_t>(exists ? qrow[0] : 0) * p.heads + (lane < p.heads ? lane : 0)];
+  if (!exists || lane >= p.heads) wv = 0.0f;
+  wbuf[0][lane] = wv;
+  out[0] = row_out(p.logits + static_cast<int64_t>(gd.row0 + wave) * p.logits_stride + gd.col0, exists ? L[wave] : 0);
+  __builtin_amdgcn_wave_barrier();
+  const int hg = 4 * (lane >> 5);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 x = *reinterpret_cast<const float4*>(&wbuf[0][32 * mt + 8 * i4 + hg]);
+      wf.v[0][mt][4 * i4 + 0] = x.x;
+      wf.v[0][mt][4 * i4 + 1] = x.y;
+      wf.v[0][mt][4 * i4 + 2] = x.z;
+      wf.v[0][mt][4 * i4 + 3] = x.w;
+    }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Waits (wave 0) until page j has landed, given how many pages were
+// requested after it.
+template <int D, bool MX>
+__device__ __forceinline__ void wait_ring_page(int after) {
+  constexpr int n = Geometry<D, MX>::kLoads;
+  static_assert(kRing == 4, "the waits below cover up to kRing - 2 later pages");
+  if (after >= 2) wait_vmcnt<2 * n>();
+  else if (after == 1) wait_vmcnt<n>();
+  else wait_all_loads();
+}
+
+template <int D, bool MX, int MT>
+__global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(ScoreParams p) {
+  constexpr int NT = kBlockRows * kWave;
+  __shared__ BlockShared<D, MX> sm;
+  const RowArgs& R = p.rows;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int NG = build_request_tables<kBlockRows, NT>(R, sm);
+  build_page_prefix<kBlockRows, NT>(R, sm, NG);
+  const int64_t P = sm.page_prefix[NG];
+
+  // this workgroup's contiguous page range (the same for all its waves)
+  const int j0 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * blockIdx.x / gridDim.x));
+  const int j1 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * (blockIdx.x + 1) / gridDim.x));
+  if (j0 >= j1) return;
+
+  const bool issuer = wave == 0;
+  bool bad_page = false;
+  int jb = j0;
+  int ids = issuer ? page_ids<kBlockRows>(p, sm.page_prefix, sm.req_tab, NG, jb, j1) : 0;
+  auto id_of = [&](int j) -> int {  // wave 0 only; j < j1
+    if (j - jb >= kWave) {
+      jb = j;
+      ids = page_ids<kBlockRows>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+    }
+    const int id = __builtin_amdgcn_readlane(ids, j - jb);
+    const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
+    bad_page |= !ok;  // ids outside the pool read page 0 and are reported
+    return ok ? id : 0;
+  };
+
+  QFrag<D, 1, MT> qf;
+  WFrag<1, MT> wf;
+  RowOut out[1];
+  int gs = group_of_page(sm.page_prefix, NG, j0);
+  setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
+  int g_first = sm.page_prefix[gs];
+
+  if (issuer) {
+    int first[kRing - 1];
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) first[i] = j0 + i < j1 ? id_of(j0 + i) : 0;
+    wait_all_loads();  // nothing the compiler loaded before is still in flight
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i)
+      if (j0 + i < j1) dma_page<D, MX>(p, first[i], lds_addr(sm.ring[i]));
+    wait_ring_page<D, MX>((j0 + kRing - 2 < j1 - 1 ? j0 + kRing - 2 : j1 - 1) - j0);  // page j0 has landed
+  }
+  __syncthreads();
+  decode_page_slice<D, MX>(sm.ring[0], sm.dec[0], wave);
+
+  // Per page j: one barrier publishes raw page j + 1 and decoded page j and
+  // frees the buffers of page j - 1; then page j + kRing - 1 is requested,
+  // page j + 1 decoded, and page j scored.  Scoring is software-pipelined
+  // over 32-key tiles: the MFMAs of a tile are issued next to the head sums
+  // of the tile before it (independent work the SIMD overlaps), alternating
+  // between two accumulator sets.  The range is walked one group at a time,
+  // so that setting up a row stays out of the page loop.
+  const int key_off = (lane & 31) * 4;
+  v16f acc0[MT], acc1[MT];
+  float ks0 = 0.0f, ks1 = 0.0f;
+  int j = j0;
+  for (;;) {
+    const int seg_end = sm.page_prefix[gs + 1] < j1 ? sm.page_prefix[gs + 1] : j1;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc1[mt] = v16f{};
+    int off1 = 0x7FFFFFF0;  // byte offset of the pending tile 1 (none yet)
+    for (; j < seg_end; ++j) {
+      const int i = j - j0;  // page j0 + i sits in raw buffer i % kRing, decoded buffer i % 2
+      if (issuer && j + 1 < j1) {
+        const int last = j + kRing - 2 < j1 - 1 ? j + kRing - 2 : j1 - 1;
+        wait_ring_page<D, MX>(last - (j + 1));  // raw page j + 1 has landed
+      }
+      __syncthreads();
+      if (issuer && j + kRing - 1 < j1) {
+        const int nxt = id_of(j + kRing - 1);
+        dma_page<D, MX>(p, nxt, lds_addr(sm.ring[(i + kRing - 1) % kRing]));
+      }
+      if (j + 1 < j1) decode_page_slice<D, MX>(sm.ring[(i + 1) % kRing], sm.dec[(i + 1) & 1], wave);
+      const v8bf* dec = sm.dec[i & 1];
+      const uint8_t* raw = sm.ring[i % kRing];
+      const int base = (j - g_first) * kPage * 4 + key_off;
+      tile_mfma<D, MX, MT>(dec, raw, 0, qf, acc0, ks0);
+      tile_logits<MT>(acc1, ks1, wf, out[0], off1);
+      __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
+      tile_mfma<D, MX, MT>(dec, raw, 1, qf, acc1, ks1);
+      tile_logits<MT>(acc0, ks0, wf, out[0], base);
+      __builtin_amdgcn_sched_barrier(0);
+      off1 = base + 32 * 4;
+    }
+    tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the segment's last tile
+    if (j >= j1) break;
+    gs = advance_group(sm.page_prefix, gs, j);
+    setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
+    g_first = sm.page_prefix[gs];
   }
   wait_all_loads();  // no request may still be writing LDS when the wave ends
   if (bad_page && lane == 0) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, kStatusBadPage);
