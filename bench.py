@@ -19,7 +19,16 @@ the per-launch durations used for the roofline.
 
 Prints one JSON line.  `--summarize-prof DIR...` turns rocprofv3 outputs
 (kernel-trace stats and FETCH_SIZE / WRITE_SIZE counter runs) into
-profiles/decode_fused_fp8_c2.{md,json}, which later runs use for `traffic`.
+profiles/score_kernel_fp8_decode_32req.{md,json}, which later runs use for
+`traffic`.
+
+`--prefill` measures the prefill path instead (a separate line, not the
+benchmark's value): the chunks the planner makes for the prefill workload
+(2 requests x 16384 queries over 65536 keys, H=64, D=128, top-k 2048), each
+scored by idx_logits_paged on its rows and selected by idx_topk; the scorer
+is reported against the bf16 dense MFMA peak.  `--summarize-prefill` turns
+its rocprofv3 kernel-trace and SQ-counter runs into
+profiles/score_block_kernel_fp8_prefill.md.
 """
 
 from __future__ import annotations
@@ -37,6 +46,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "index keys scored/sec + top-k rows/sec, 1×MI355X; % of HBM (decode) / MFMA (prefill) peak"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PREFILL_KERNEL_SUBSTR = "score_block_kernel<128, false, 2>"
+PREFILL_PROFILE_NAME = "score_block_kernel_fp8_prefill"
 PROFILE_NAME = "score_kernel_fp8_decode_32req"
 KERNEL_SUBSTR = "score_kernel<128, false, 1, 2>"   # scorer: D=128, fp8, 1 row/group, 64 heads
 TOPK_SUBSTR = "topk_kernel<"
@@ -251,6 +263,131 @@ def run(args):
     print(json.dumps(res), flush=True)
 
 
+def run_prefill(args):
+    """The prefill workload's planner chunks: per chunk one scorer and one
+    selector launch over all of its rows."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_decode_amd as idx
+    from workloads import config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = config("C5")
+    cache = idx.Cache(torch.from_numpy(wl.cache).to(dev), wl.head_dim, wl.fmt)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    seq = torch.from_numpy(wl.seq_lens).to(dev)
+    qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(wl.query_lens)]).astype(np.int32)).to(dev)
+    q = torch.from_numpy(wl.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(wl.w).to(dev)
+    k = wl.topk
+    recs = idx.idx_prefill_chunks(wl.seq_lens, wl.query_lens, 65536, 512 << 20)
+    chunks = []
+    flops = 0
+    n_rows = 0
+    for rec in recs:
+        b0, b1 = rec["req_begin"], rec["req_end"]
+        rows = idx.Rows.prefill(bt[b0:b1], seq[b0:b1], qsl[b0:b1 + 1], rec["q_begin"], rec["q_end"],
+                                int(wl.seq_lens[b0:b1].max()))
+        M, N = rec["q_end"] - rec["q_begin"], rec["total_seq_lens"]
+        chunks.append((rows, q[rec["token_begin"]:rec["token_end"]], w[rec["token_begin"]:rec["token_end"]], M, N))
+        # keys per row: L = seq_len - query_len + j + 1 for query j of its request
+        for b in range(b0, b1):
+            qs = int(wl.query_lens[b])
+            j = np.arange(qs)
+            lo = max(0, rec["q_begin"] - int(np.sum(wl.query_lens[b0:b])))
+            hi = min(qs, rec["q_end"] - int(np.sum(wl.query_lens[b0:b])))
+            L = int(wl.seq_lens[b]) - qs + j[lo:hi] + 1
+            flops += int(L.sum()) * 2 * wl.heads * wl.head_dim
+            n_rows += max(0, hi - lo)
+    big = max(M * N for _, _, _, M, N in chunks)
+    logits_buf = torch.empty(big, dtype=torch.float32, device=dev)
+    outs = torch.empty((max(c[3] for c in chunks), k), dtype=torch.int32, device=dev)
+    ws = idx.new_workspace(4096, dev)
+    stream = torch.cuda.current_stream()
+
+    def one_pass(ev=None):
+        for ci, (rows, qq, ww, M, N) in enumerate(chunks):
+            lg = logits_buf[: M * N].view(M, N)
+            if ev is not None:
+                ev[ci][0].record(stream)
+            idx.idx_logits_paged(cache, rows, qq, ww, lg, ws, stream)
+            if ev is not None:
+                ev[ci][1].record(stream)
+            idx.idx_topk(lg, rows, k, outs[:M], ws, stream)
+            if ev is not None:
+                ev[ci][2].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in chunks]
+    one_pass(evs)
+    torch.cuda.synchronize()
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    topk_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
+    tflops = flops / (score_ms * 1e-3) / 1e12
+    res = {
+        "metric": "prefill indexer: query rows scored and selected per second, 1xMI355X",
+        "value": n_rows / wall, "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill: 2 requests x 16384 queries, seq_len 65536, H=64, head_dim 128, "
+                               "top-k 2048, fp8 keys; planner chunks of <= 65536 keys and <= 512 MiB of logits",
+                   "name": wl.name, "chunks": len(chunks), "rows": n_rows},
+        "scorer_ms_per_pass": score_ms, "topk_ms_per_pass": topk_ms,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None, "algorithmic_flops_per_pass": flops,
+                     "kernel": "score_block_kernel<D=128, fp8, 64 heads> (idx_logits_paged on prefill rows)"},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def summarize_prefill(stats_dir, pmc_dir, commands, bench_json):
+    """Kernel time and SQ counters of the prefill scorer ->
+    profiles/score_block_kernel_fp8_prefill.md"""
+    import numpy as np
+
+    stats = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    lines = []
+    for r in _csv_rows(stats[0]):
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for r in _csv_rows(files[0]):
+        if PREFILL_KERNEL_SUBSTR not in r.get("Kernel_Name", ""):
+            continue
+        per.setdefault(r["Dispatch_Id"], {}).setdefault(r["Counter_Name"], 0.0)
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    names = sorted({c for d in per.values() for c in d})
+    med = {c: float(np.median([d[c] for d in per.values() if c in d])) for c in names}
+    with open(bench_json) as f:
+        bl = json.loads(f.read().strip().splitlines()[-1])
+    md = ["# Prefill scorer on the prefill workload (2 x 16384 queries over 65536 keys, H=64, D=128)", "",
+          "Commands (run from the repository root on one MI355X):", ""]
+    md += [f"    {c}" for c in commands]
+    md += ["", "## rocprofv3 --kernel-trace --stats", "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"] + lines
+    md += ["", "## bench.py --prefill", "",
+           f"- scorer {bl['scorer_ms_per_pass']:.2f} ms per pass of {bl['config']['chunks']} chunks (HIP events) = "
+           f"{bl['roofline']['achieved']:.0f} TFLOP/s of algorithmic bf16 work = "
+           f"{bl['roofline']['frac'] * 100:.1f} % of the 2.5 PFLOP/s dense bf16 peak",
+           f"- selector {bl['topk_ms_per_pass']:.2f} ms per pass; {bl['value']:.4g} rows/s end to end",
+           "", "## SQ counters of one scorer dispatch (rocprofv3 --pmc, summed over the chip; median over dispatches)",
+           ""] + [f"- {c}: {med[c]:.4g}" for c in names]
+    md += [f"", f"- kernel source hash {kernel_source_hash()}"]
+    with open(os.path.join(ROOT, "profiles", PREFILL_PROFILE_NAME + ".md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 output -> profiles/
 # ---------------------------------------------------------------------------
@@ -364,14 +501,22 @@ def main():
     ap.add_argument("--summarize-prof", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--bench-json", default=None)
+    ap.add_argument("--prefill", action="store_true", help="measure the prefill path instead (separate line)")
+    ap.add_argument("--summarize-prefill", nargs=2, metavar=("STATS_DIR", "PMC_DIR"))
     args = ap.parse_args()
     if args.summarize_prof:
         summarize(args.summarize_prof, args.commands, args.bench_json)
+        return
+    if args.summarize_prefill:
+        summarize_prefill(args.summarize_prefill[0], args.summarize_prefill[1], args.commands, args.bench_json)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (multi-GPU sharding is "
                                    "described, not implemented)"}), flush=True)
         sys.exit(2)
+    if args.prefill:
+        run_prefill(args)
+        return
     run(args)
 
 
