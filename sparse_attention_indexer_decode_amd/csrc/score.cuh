@@ -1,19 +1,22 @@
 // Paged indexer scorer for gfx950:
 //   logit[r, t] = scale_t * sum_h w[r,h] * relu(q[r,h,:] . code_t)   (t < L_r)
 //
+// Two kernels share the helpers below: score_kernel for decode rows and
+// score_block_kernel (at the end of this file) for prefill rows.
+//
 // Work decomposition.  Rows are bundled into "groups" of up to RG rows that
 // share one request (the next_n decode rows of a request, or consecutive
 // query rows of a prefill request); a group reads its request's pages once
-// for all its rows.  Every workgroup (one per CU, eight waves) builds the
-// prefix of pages over groups in LDS from the device lengths (the host never
-// reads them); the global page list is then cut into equal contiguous ranges,
-// one per wave.
+// for all its rows.  Every workgroup (one per CU) builds the prefix of pages
+// over groups in LDS from the device lengths (the host never reads them);
+// the global page list is then cut into equal contiguous ranges, one per
+// wave (decode) or one per workgroup (prefill).
 //
-// Memory pipeline.  Each wave streams its pages through a two-page ring in
-// LDS filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KiB per
-// instruction): while page j is scored from one buffer, page j+1 is already
-// in flight into the other, and page j+2 is requested as soon as page j's
-// buffer is consumed.  No staging registers are used, and the waits are
+// Decode memory pipeline.  Each wave streams its pages through a two-page
+// ring in LDS filled by direct global->LDS loads (global_load_lds_dwordx4,
+// 1 KiB per instruction): while page j is scored from one buffer, page j+1 is
+// already in flight into the other, and page j+2 is requested as soon as
+// page j's buffer is consumed.  No staging registers are used, and the waits are
 // explicit vmcnt counts (loads retire in order; every wait leaves exactly the
 // loads issued after the page it needs outstanding).
 //
