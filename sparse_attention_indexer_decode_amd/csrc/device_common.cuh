@@ -138,6 +138,45 @@ __device__ __forceinline__ float block_max(float v, int* sm) {
   return r;
 }
 
+// Block-wide min and max of a float over NT threads (NaNs are ignored, as
+// by fminf / fmaxf) with one barrier: DPP within 16-lane rows, lane reads
+// across the rows, one LDS slot per wave.  `sm` holds 2 NT/64 ints that no
+// thread may write again before the caller's next barrier.
+template <int NT>
+__device__ __forceinline__ void block_min_max(float& lo, float& hi, int* sm) {
+  auto dpp = [](float v, int ctrl) -> float {
+    const int i = __float_as_int(v);
+    switch (ctrl) {
+      case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+      case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x141, 0xF, 0xF, false));  // row_half_mirror
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x140, 0xF, 0xF, false));  // row_mirror
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ctrl = c == 0 ? 0xB1 : c == 1 ? 0x4E : c == 2 ? 0x141 : 0x140;
+    lo = fminf(lo, dpp(lo, ctrl));
+    hi = fmaxf(hi, dpp(hi, ctrl));
+  }
+  auto lane_f = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  lo = fminf(fminf(lane_f(lo, 0), lane_f(lo, 16)), fminf(lane_f(lo, 32), lane_f(lo, 48)));
+  hi = fmaxf(fmaxf(lane_f(hi, 0), lane_f(hi, 16)), fmaxf(lane_f(hi, 32), lane_f(hi, 48)));
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sm[wid] = __float_as_int(lo);
+    sm[NT / kWave + wid] = __float_as_int(hi);
+  }
+  __syncthreads();
+  lo = __int_as_float(sm[0]);
+  hi = __int_as_float(sm[NT / kWave]);
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) {
+    lo = fminf(lo, __int_as_float(sm[w]));
+    hi = fmaxf(hi, __int_as_float(sm[NT / kWave + w]));
+  }
+}
+
 __device__ __forceinline__ int block_sum_int(int v, int* sm, int nt) {
   // generic block sum for any multiple-of-64 block size
   const int lane = threadIdx.x & (kWave - 1);

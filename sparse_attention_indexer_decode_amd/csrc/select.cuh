@@ -7,16 +7,23 @@
 // written in ascending position order.
 //
 // Keys: floats map to order-preserving 32-bit keys (-0.0 folded onto +0.0).
-// Digits: d1 = key[31:20] (4096 bins), then key[19:10] and key[9:0].
+// Digits of the radix passes: d1 = key[31:20] (4096 bins), then key[19:10]
+// and key[9:0].
 //
-// Rows of up to kRowCap keys (the common case) are resident in LDS:
-//   1. the whole row is requested at once with direct global->LDS loads;
-//   2. three LDS histogram passes (d1, then the two lower digits among the
-//      keys matching the prefix so far) fix the threshold key T and how many
-//      keys equal to T are taken (`need`, the lowest positions);
-//   3. ordered emission: each wave owns a run of 64-key blocks; per block a
-//      ballot of "above T" and "equal to T" gives, with the wave's running
-//      counts and one scan over the waves, every winner's output slot.
+// Rows of up to kRowCap keys (the common case) stay in registers, 32 keys
+// (eight 16-byte quads) per thread (select_row_reg):
+//   1. the whole row is loaded at once; one block reduction gives its min and
+//      max;
+//   2. first digit = a linear map of the value onto 4096 bins between min and
+//      max (monotone, so the bin order is the value order); an LDS histogram
+//      gives the bin B1 holding the k-th largest;
+//   3. keys above B1 go straight into an LDS bitmap over positions (a quad's
+//      4 keys form a nibble, eight lanes OR theirs into a 32-bit word); the
+//      keys of bin B1 go to a short list (position and key);
+//   4. the winners of bin B1 are decided exactly (pairwise ranks for a short
+//      list, radix passes on the 32-bit key and then on positions otherwise)
+//      and added to the bitmap;
+//   5. one ordered scan over the bitmap writes the k positions.
 // Longer rows stream from global memory:
 //   1. d1 histogram of the row in LDS, one pass with many coalesced loads in
 //      flight.
@@ -135,7 +142,9 @@ __device__ __forceinline__ int strided_pos(int base, int j) {
 
 // Finds the digit bin holding the need-th largest element among `nbins`
 // bins read through `bin(d)`; returns (digit, count above it, count in it).
-template <int NT, class BinFn>
+// Without the trailing barrier the caller must not write sm.bc[0..2] or
+// sm.scan before its next barrier.
+template <int NT, bool kTrailingSync = true, class BinFn>
 __device__ __forceinline__ void find_digit(int nbins, int need, BinFn bin, SelectShared<NT>& sm, int& digit,
                                            int& above_out, int& cnt_out) {
   const int tid = threadIdx.x;
@@ -162,7 +171,7 @@ __device__ __forceinline__ void find_digit(int nbins, int need, BinFn bin, Selec
   digit = sm.bc[0];
   above_out = sm.bc[1];
   cnt_out = sm.bc[2];
-  __syncthreads();
+  if (kTrailingSync) __syncthreads();
 }
 
 // d1 histogram of a row into sm.u.hist1.
@@ -438,8 +447,7 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
     }
   }
   for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
-  lo = block_min<NT>(lo, sm.scan);
-  hi = block_max<NT>(hi, sm.scan);
+  block_min_max<NT>(lo, hi, sm.hist2);  // hist2 is free until the exact resolution
   // bin(v) = clamp(fma(v, a, b), 0, 4095) truncated, with a = 4096 / (hi - lo)
   // and b = -lo a: one rounding of (v - lo) a, so monotone non-decreasing in
   // v.  (hi - lo is formed from halves so that it cannot overflow; when a or
@@ -467,10 +475,12 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
   }
   __syncthreads();
   int B1, above1, cnt1;
-  find_digit<NT>(kD1Bins, k, [&](int d) { return sm.u.hist1[d]; }, sm, B1, above1, cnt1);
+  if (tid == 0) sm.bc[4] = 0;  // eq-list counter, published by find_digit's barrier
+  find_digit<NT, false>(kD1Bins, k, [&](int d) { return sm.u.hist1[d]; }, sm, B1, above1, cnt1);
   if (cnt1 > kCandCap) {
     // too many keys in the threshold bin (large ties): radix-select from
     // global memory
+    __syncthreads();  // every thread has read find_digit's result
     select_row_stream<NT>(row, L, k, out, sm);
     return;
   }
@@ -480,11 +490,9 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
   //    consecutive lanes (q % 8 == lane % 8), and an OR over those lanes
   //    gives the word, stored by its first lane.  Keys in bin B1 go to a
   //    short list (positions only) for the exact decision.
-  uint32_t* bits = sm.u.sel;  // hist1 is dead once B1 is known
+  uint32_t* bits = sm.u.sel;  // hist1 is dead once B1 is known (every thread has passed find_digit's barrier)
   int* eq_pos = sm.c.cidx;
   uint32_t* eq_key = sm.c.ckey;
-  if (tid == 0) sm.bc[4] = 0;
-  __syncthreads();
   const int need = k - above1;  // keys of bin B1 to take
 #pragma unroll
   for (int j = 0; j < EQ; ++j) {
@@ -504,8 +512,12 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
       while (eq) {
         const int e = __builtin_ctz(eq);
         eq &= eq - 1u;
+        const float v = e == 0 ? x[4 * j] : e == 1 ? x[4 * j + 1] : e == 2 ? x[4 * j + 2] : x[4 * j + 3];
         const int slot = atomicAdd(&sm.bc[4], 1);
-        if (slot < kCandCap) eq_pos[slot] = 4 * q + e;
+        if (slot < kCandCap) {
+          eq_pos[slot] = 4 * q + e;
+          eq_key[slot] = ordered_key(v);
+        }
       }
     }
   }
@@ -514,8 +526,6 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
 
   // 4. the `need` winners of bin B1: largest exact key, ties to the lowest
   //    position.  Few keys: rank each against all; more: radix passes.
-  for (int i = tid; i < m; i += NT) eq_key[i] = ordered_key(row[eq_pos[i]]);
-  __syncthreads();
   if (need == m) {
     for (int i = tid; i < m; i += NT) atomicOr(&bits[eq_pos[i] >> 5], 1u << (eq_pos[i] & 31));
   } else if (m <= kRankCap) {
