@@ -150,6 +150,11 @@ __device__ __forceinline__ void find_digit(int nbins, int need, BinFn bin, Selec
   const int tid = threadIdx.x;
   const int per = nbins / NT;
   const int hi = nbins - tid * per;
+  if (tid == 0) {  // a defined result even when fewer than `need` elements are binned
+    sm.bc[0] = 0;
+    sm.bc[1] = 0;
+    sm.bc[2] = 0;
+  }
   int s = 0;
   for (int d = hi - per; d < hi; ++d) s += bin(d);
   int tot;
@@ -585,7 +590,8 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
     while (sel) {
       const int bpos = __builtin_ctz(sel);
       sel &= sel - 1u;
-      out[o++] = wd * 32 + bpos;
+      if (o < k) out[o] = wd * 32 + bpos;  // never more than k, whatever the input bits
+      ++o;
     }
   }
   __syncthreads();
