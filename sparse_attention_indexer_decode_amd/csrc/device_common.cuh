@@ -191,6 +191,16 @@ __device__ __forceinline__ int block_sum_int(int v, int* sm, int nt) {
   return tot;
 }
 
+// Range [begin, end) of part `i` when `total` items are split into `parts`
+// contiguous ranges of floor or ceil(total / parts) items (the first
+// total % parts get one more).  32-bit arithmetic: one unsigned division.
+__device__ __forceinline__ void even_split(uint32_t total, uint32_t parts, uint32_t i, int& begin, int& end) {
+  const uint32_t q = total / parts;
+  const uint32_t r = total - q * parts;
+  begin = static_cast<int>(q * i + (i < r ? i : r));
+  end = begin + static_cast<int>(q) + (i < r ? 1 : 0);
+}
+
 // Key count of grid row (b, i) of a decode batch: position + 1 for real
 // tokens, 0 for padded slots; clamped to [0, max_len].
 __device__ __forceinline__ int decode_row_len(int seq, int dl, int i, int max_len) {

@@ -270,14 +270,16 @@ __device__ __forceinline__ void load_query(const ScoreParams& p, const int (&qlo
 
 // The same fragments for D = 128 and heads = 32 MT, read through the wave's
 // idle LDS area.  Loaded directly, each 16-byte fragment load of a wave
-// touches 64 different 128-byte lines (32 heads x 2 lane halves); here every
-// load instruction reads 1 KiB of contiguous query (4 heads), the 16-byte
-// chunks are written to LDS, and the fragments are read back.  Chunk c of
-// head h (dims 8c .. 8c + 7, within row r's block) sits at 16-byte slot
-// 16 h + (c ^ (h % 16) ^ ((h / 16) % 2)): the XOR keeps the 16 (or 32)
-// lanes of each b128 access on distinct bank groups, for the writes (one
-// head per 16 lanes) and the fragment reads (one head per lane) alike.
-// The caller must not reuse the area before the reads have returned.
+// touches 64 different 128-byte lines (32 heads x 2 lane halves).  Here
+// direct global->LDS loads copy the group's query block into the area, each
+// instruction 1 KiB of contiguous query (4 heads), and the fragments are
+// read back from LDS.  Chunk c of head h (dims 8c .. 8c + 7, within row r's
+// block) sits at 16-byte slot 16 h + (c ^ (h % 16) ^ ((h / 16) % 2)): the
+// XOR keeps the 16 (or 32) lanes of each b128 fragment read on distinct
+// bank groups.  The load writes lane l's 16 bytes to slot 64 i + l, so lane
+// l fetches the chunk that belongs there, a permutation within the same
+// 1 KiB.  Waits for every outstanding load before reading; the caller must
+// not reuse the area before the reads have returned.
 template <int D, int RG, int MT>
 __device__ __forceinline__ void load_query_staged(const ScoreParams& p, const int (&qload)[RG], uint8_t* area,
                                                   QFrag<D, RG, MT>& f) {
@@ -285,21 +287,22 @@ __device__ __forceinline__ void load_query_staged(const ScoreParams& p, const in
   constexpr int kHeads = 32 * MT;
   constexpr int kLoads = kHeads * D * 2 / 1024;  // 1 KiB per load instruction
   const int lane = lane_id();
-  auto slot = [](int h, int c) { return 16 * h + (c ^ (h & 15) ^ ((h >> 4) & 1)); };
-  u32x4 v[RG][kLoads];
+  auto swz = [](int h) { return (h & 15) ^ ((h >> 4) & 1); };
+  const uint32_t base = lds_addr(area);
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + static_cast<int64_t>(qload[r] >= 0 ? qload[r] : 0) * kHeads * D);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.q) +
+                         static_cast<int64_t>(qload[r] >= 0 ? qload[r] : 0) * kHeads * D * 2;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) v[r][i] = src[64 * i + lane];
+    for (int i = 0; i < kLoads; ++i) {
+      const int h = 4 * i + lane / 16;
+      const int c = (lane % 16) ^ swz(h);
+      lds_dma16(src + (16 * h + c) * 16, base + r * kHeads * 256 + 1024 * i);
+    }
   }
+  wait_all_loads();
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  lds_u32x4* st = (lds_u32x4*)area;  // LDS accesses, whatever the compiler infers
-#pragma unroll
-  for (int r = 0; r < RG; ++r)
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) st[r * kHeads * 16 + slot(4 * i + lane / 16, lane % 16)] = v[r][i];
-  __builtin_amdgcn_wave_barrier();
+  const lds_u32x4* st = (const lds_u32x4*)area;  // LDS accesses, whatever the compiler infers
   const int m = lane & 31;
   const int g = lane >> 5;
 #pragma unroll
@@ -307,8 +310,10 @@ __device__ __forceinline__ void load_query_staged(const ScoreParams& p, const in
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        f.a[r][mt][s] = __builtin_bit_cast(v8bf, st[r * kHeads * 16 + slot(32 * mt + m, 8 * g + s)]);
+      for (int s = 0; s < D / 16; ++s) {
+        const int h = 32 * mt + m;
+        f.a[r][mt][s] = __builtin_bit_cast(v8bf, st[r * kHeads * 16 + 16 * h + ((8 * g + s) ^ swz(h))]);
+      }
 }
 
 // max(x, 0) in one instruction: as signed integers, negative floats
@@ -555,6 +560,10 @@ __device__ __forceinline__ void setup_group(const ScoreParams& p, const int (*re
   int L[RG], ql[RG];
   bool rl[RG];
   const GroupDesc gd = describe_group<RG>(R, req_tab, g, group_request<RG>(R, req_tab, g), L, ql, rl);
+  // weights first: they land with (not after) the queries
+  float wv[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) wv[r] = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
   if constexpr (query_stage_bytes<D, RG, MT>() > 0) {
     if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, RG, MT>(p, ql, stage, qf);
     else load_query<D, RG, MT>(p, ql, qf);
@@ -563,9 +572,7 @@ __device__ __forceinline__ void setup_group(const ScoreParams& p, const int (*re
   }
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
-    float wv = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
-    if (!rl[r] || lane >= p.heads) wv = 0.0f;
-    wbuf[r][lane] = wv;
+    wbuf[r][lane] = (!rl[r] || lane >= p.heads) ? 0.0f : wv[r];
     out[r] = row_out(p.logits + static_cast<int64_t>(gd.row0 + r) * p.logits_stride + gd.col0,
                      r < gd.nrows ? L[r] : 0);
   }
@@ -602,10 +609,10 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
   const int P = sm.page_prefix[NG];
 
   // this wave's contiguous page range
-  const int64_t NW = static_cast<int64_t>(gridDim.x) * kScoreWaves;
-  const int64_t W = static_cast<int64_t>(blockIdx.x) * kScoreWaves + __builtin_amdgcn_readfirstlane(wave);
-  const int j0 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * W / NW));
-  const int j1 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * (W + 1) / NW));
+  int j0, j1;
+  even_split(P, gridDim.x * kScoreWaves, blockIdx.x * kScoreWaves + __builtin_amdgcn_readfirstlane(wave), j0, j1);
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
 
   float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
   WaveArea<D, MX, RG, MT>& area = sm.area[wave];
@@ -798,11 +805,13 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
   const int lane = tid & 63;
   const int NG = build_request_tables<kBlockRows, NT>(R, sm);
   build_page_prefix<kBlockRows, NT>(R, sm, NG);
-  const int64_t P = sm.page_prefix[NG];
+  const int P = sm.page_prefix[NG];
 
   // this workgroup's contiguous page range (the same for all its waves)
-  const int j0 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * blockIdx.x / gridDim.x));
-  const int j1 = __builtin_amdgcn_readfirstlane(static_cast<int>(P * (blockIdx.x + 1) / gridDim.x));
+  int j0, j1;
+  even_split(P, gridDim.x, blockIdx.x, j0, j1);
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
   if (j0 >= j1) return;
 
   const bool issuer = wave == 0;
