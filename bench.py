@@ -13,9 +13,10 @@ Timing: inputs are resident in HBM before the timed region.  The pool
 (169 MB) would fit the 256 MiB MALL, so each step reads one of `--copies`
 identical pools in rotation (8 x 169 MB by default); between two uses of a
 pool ~550 MB of other keys stream through, so the keys come from HBM.  K
-steps are bracketed by synchronisation (the value); the same K steps are
-then run with HIP events on the launch stream around each launch, which give
-the per-launch durations used for the roofline.
+steps are bracketed by synchronisation (the value).  Then each kernel is
+launched K times back to back (the scorer still on the rotated pools)
+between HIP events on the launch stream; the mean interval per launch is the
+launch duration used for the roofline.
 
 Prints one JSON line.  `--summarize-prof DIR...` turns rocprofv3 outputs
 (kernel-trace stats and FETCH_SIZE / WRITE_SIZE counter runs) into
@@ -202,16 +203,28 @@ def run(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert torch.equal(first, outs), "decode top-k is not deterministic across steps"
-    # the same K steps again with HIP events on the launch stream around each
-    # of the two launches (per-kernel durations for the roofline; the events
-    # themselves cost a few us per step, so the value above is taken without)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # per-kernel launch durations for the roofline: HIP events on the launch
+    # stream around K back-to-back launches of one kernel (the scorer on the
+    # rotated pools, the selector on the step's logits), divided by K, in
+    # chunks so that min and spread are visible
+    def timed(fn, n, chunk=20):
+        per = []
+        for c0 in range(0, n, chunk):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            m = min(chunk, n - c0)
+            e0.record(stream)
+            for i in range(m):
+                fn(c0 + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / m)
+        return per
+
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    score_ms = timed(lambda i: idx.idx_logits_paged(caches[(args.warmup + i) % len(caches)], rows, q, w, logits, ws,
+                                                    stream), args.steps)
+    topk_ms = timed(lambda i: idx.idx_topk(logits, rows, k, outs, ws, stream), args.steps)
     torch.cuda.synchronize()
-    score_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
     assert torch.equal(first, outs), "decode top-k is not deterministic across steps"
 
     # warm-MALL reference: the same pool back to back (context only)
@@ -469,9 +482,10 @@ def summarize(dirs, commands, bench_json=None):
     md += ["", "## rocprofv3 --kernel-trace --stats", "",
            "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"] + lines
     if bl is not None:
-        md += ["", "## HIP-event launch durations in the same benchmark (bench.py, 200 timed steps)", "",
+        md += ["", "## HIP-event launch durations in the same benchmark (bench.py: 200 back-to-back launches of each "
+               "kernel between events, mean per launch)", "",
                f"- scorer {bl['scorer_ms_avg'] * 1e3:.2f} us per launch (rocprofv3 kernel time "
-               f"{out.get('avg_ns', float('nan')) / 1e3:.2f} us; the events also hold the dispatch of the launch)",
+               f"{out.get('avg_ns', float('nan')) / 1e3:.2f} us; the events also hold the gap between launches)",
                f"- selector {bl['topk_ms_avg'] * 1e3:.2f} us per launch (rocprofv3 "
                f"{out.get('topk_avg_ns', float('nan')) / 1e3:.2f} us)",
                f"- step {bl['ms_per_step'] * 1e3:.2f} us wall clock; {bl['value']:.4g} keys/s; scorer "
