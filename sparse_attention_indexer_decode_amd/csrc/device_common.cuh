@@ -74,12 +74,6 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Number of set bits of m below this lane.
-__device__ __forceinline__ int mbcnt64(uint64_t m) {
-  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-}
-
 // Wave-wide inclusive prefix sum (DPP: shifts within 16-lane rows, then
 // row broadcasts of lanes 15 and 31).
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
@@ -112,30 +106,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int& total, int* sm) 
   __syncthreads();
   total = tot;
   return before + x - v;
-}
-
-// Block-wide min / max of a float over NT threads (`sm` holds NT/64 ints).
-template <int NT>
-__device__ __forceinline__ float block_min(float v, int* sm) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v = fminf(v, __shfl_xor(v, d, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0) sm[threadIdx.x / kWave] = __float_as_int(v);
-  __syncthreads();
-  float r = __int_as_float(sm[0]);
-  for (int w = 1; w < NT / kWave; ++w) r = fminf(r, __int_as_float(sm[w]));
-  __syncthreads();
-  return r;
-}
-template <int NT>
-__device__ __forceinline__ float block_max(float v, int* sm) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0) sm[threadIdx.x / kWave] = __float_as_int(v);
-  __syncthreads();
-  float r = __int_as_float(sm[0]);
-  for (int w = 1; w < NT / kWave; ++w) r = fmaxf(r, __int_as_float(sm[w]));
-  __syncthreads();
-  return r;
 }
 
 // Block-wide min and max of a float over NT threads (NaNs are ignored, as
