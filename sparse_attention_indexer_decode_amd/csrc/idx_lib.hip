@@ -22,6 +22,7 @@ idx_status fail(idx_status st, const char* what) {
 }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreadsLean = 512;
 
 int row_bytes(int fmt, int d) { return fmt == IDX_FMT_FP8_E4M3 ? d + 4 : d / 2 + d / 32; }
 
@@ -202,7 +203,13 @@ idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, in
   p.rows = R;
   p.k = k;
   p.out = out;
-  hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0, s, p);
+  // Batches whose rows may exceed the register path and that have at least
+  // two rows per CU run a streaming-only 512-thread kernel, several rows per
+  // CU at once; otherwise one 1024-thread workgroup per row.
+  if (R.max_len > kRowCap && R.num_rows >= 2 * device_cu_count())
+    hipLaunchKernelGGL((topk_kernel<kTopkThreadsLean, false>), dim3(R.num_rows), dim3(kTopkThreadsLean), 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0, s, p);
   return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
 }
 

@@ -597,12 +597,14 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
   __syncthreads();
 }
 
-// Top-k of one row.
-template <int NT>
+// Top-k of one row.  kReg = false leaves the register path out (every row
+// longer than k streams from memory), for a lean kernel that fits several
+// workgroups per CU.
+template <int NT, bool kReg = true>
 __device__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out, SelectShared<NT>& sm) {
   if (L <= k) {
     for (int j = threadIdx.x; j < k; j += NT) out[j] = (j < L) ? j : -1;
-  } else if (L <= kRowCap) {
+  } else if (kReg && L <= kRowCap) {
     select_row_reg<NT, kRowCap / NT>(row, L, k, out, sm);
   } else {
     select_row_stream<NT>(row, L, k, out, sm);

@@ -14,7 +14,8 @@ struct TopkParams {
   int32_t* out;
 };
 
-template <int NT>
+// kReg: see select_row.
+template <int NT, bool kReg = true>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   __shared__ SelectShared<NT> sm;
   __shared__ int info[2];
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     L = seq - qlen + j + 1;
     L = L < 0 ? 0 : (L > seq ? seq : L);
   }
-  select_row<NT>(p.logits + static_cast<int64_t>(r) * p.stride + col0, L, p.k,
+  select_row<NT, kReg>(p.logits + static_cast<int64_t>(r) * p.stride + col0, L, p.k,
                  p.out + static_cast<int64_t>(r) * p.k, sm);
 }
 

@@ -125,6 +125,44 @@ def test_topk_bitexact_on_given_logits(k):
         assert np.array_equal(got[r], exp), f"row {r} (L={lens[r]}) differs"
 
 
+@pytest.mark.parametrize("k", [64, 2048])
+def test_topk_bitexact_many_rows_with_long_ones(k):
+    """A batch with at least two rows per CU and rows past the register
+    path: the selector runs its streaming-only kernel (several rows per CU)
+    on every row, short ones included."""
+    rng = np.random.default_rng(17)
+    base = [0, 1, k - 1, k, k + 1, 100, 1000, 5000, 33000, 3000, 20000, 32768, 32769, 9000, 12000, 40000]
+    R = 600
+    lens = [base[i % len(base)] for i in range(R)]
+    rows = []
+    for i, L in enumerate(lens):
+        kind = (i // len(base)) % 4
+        if kind == 0:
+            v = rng.standard_normal(L).astype(np.float32) * 8
+        elif kind == 1:
+            v = (rng.integers(-3, 4, size=L) * 0.125).astype(np.float32)
+            v[::7] = -0.0
+        elif kind == 2:
+            v = (rng.choice([-1.0, 1.0], size=L) * 10.0 ** rng.uniform(-30, 30, size=L)).astype(np.float32)
+        else:
+            v = (rng.integers(0, 50, size=L) * 0.1).astype(np.float32)
+        rows.append(v)
+    stride = max(lens) + 3
+    buf = np.full((R, stride), np.nan, dtype=np.float32)
+    for r, v in enumerate(rows):
+        buf[r, : len(v)] = v
+    d = torch.device("cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device=d)
+    bt = torch.zeros((R, 1), dtype=torch.int32, device=d)
+    rows_d = idx.Rows.decode(bt, seq, max(lens))
+    out = torch.full((R, k), -7, dtype=torch.int32, device=d)
+    idx.idx_topk(torch.from_numpy(buf).to(d), rows_d, k, out, topk_workspace(rows_d, k, d))
+    got = out.cpu().numpy()
+    for r, v in enumerate(rows):
+        exp = oracle.topk.topk_row(v.astype(np.float64), lens[r], k)
+        assert np.array_equal(got[r], exp), f"row {r} (L={lens[r]}) differs"
+
+
 def test_topk_bitexact_on_oracle_logits():
     wl = _case("fp8", 128, 64, 2, False, seed=7)
     ref = oracle.pipeline.decode_logits(wl)
