@@ -55,6 +55,15 @@ KERNEL_SUBSTR = "score_kernel<128, false, 1, 2>"   # scorer: D=128, fp8, 1 row/g
 TOPK_SUBSTR = "topk_kernel<"
 CALIB_SUBSTR = "AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float>"
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
+DECODE_WORKLOADS = {
+    "C1": "tiny fp8 decode: 1 request, L=300, 8-page pool, H=4, head_dim 32, top-k 64",
+    "C2": "fp8 decode batch: 32 requests, next_n=1, seq_len ~ U[4096, 32768], page 64, 20k-page pool, H=64, "
+          "head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
+    "C3": "MTP decode: 128 requests, next_n=2 padded grid, decode_lens in {1, 2}, seq_len log-uniform in "
+          "[512, 131072], page 64, H=64, head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
+    "C4": "MXFP4 long-context decode: 64 requests x 131072 keys, page 64, H=64, head_dim 128, top-k 2048, "
+          "e2m1 keys + ue8m0 block scales",
+}
 
 
 def kernel_source_hash() -> str:
@@ -257,10 +266,9 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "fp8 decode batch: 32 requests, next_n=1, seq_len ~ U[4096, 32768], page 64, "
-                               "20k-page pool, H=64, head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
+        "config": {"workload": DECODE_WORKLOADS[wl.name],
                    "name": wl.name, "requests": wl.num_req, "rows": R, "keys_scored": keys_scored,
-                   "cache_fmt": "fp8_e4m3", "pool_copies_rotated": args.copies},
+                   "cache_fmt": "mxfp4" if wl.fmt == "mxfp4" else "fp8_e4m3", "pool_copies_rotated": args.copies},
         "rows_per_s": R / (ms_per_step * 1e-3),
         "scorer_ms_avg": score_avg_ms,
         "scorer_ms_min": float(np.min(score_ms)),
@@ -269,7 +277,8 @@ def run(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["total"],
-                     "kernel": "score_kernel<D=128, fp8, 1 row/group, 64 heads> (idx_logits_paged)"},
+                     "kernel": f"score_kernel<D={wl.head_dim}, {wl.fmt}, {1 if wl.next_n == 1 else 2} row(s)/group, "
+                               f"{wl.heads} heads> (idx_logits_paged)"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -12,11 +12,11 @@
 // the global page list is then cut into equal contiguous ranges, one per
 // wave (decode) or one per workgroup (prefill).
 //
-// Decode memory pipeline.  Each wave streams its pages through a two-page
-// ring in LDS filled by direct global->LDS loads (global_load_lds_dwordx4,
-// 1 KiB per instruction): while page j is scored from one buffer, page j+1 is
-// already in flight into the other, and page j+2 is requested as soon as
-// page j's buffer is consumed.  No staging registers are used, and the waits are
+// Decode memory pipeline.  Each wave streams its pages through a ring of NP
+// (2-4) pages in LDS filled by direct global->LDS loads
+// (global_load_lds_dwordx4, 1 KiB per instruction): while page j is scored
+// from one buffer, pages j+1 .. j+NP-1 are already in flight, and page j+NP
+// is requested as soon as page j's buffer is consumed.  No staging registers are used, and the waits are
 // explicit vmcnt counts (loads retire in order; every wait leaves exactly the
 // loads issued after the page it needs outstanding).
 //
@@ -82,11 +82,21 @@ struct Geometry {
 template <int D, int RG, int MT>
 constexpr int query_stage_bytes() { return D == 128 ? RG * MT * 32 * D * 2 : 0; }
 
-// Each wave's LDS area: its two-page ring, which also stages the first
-// group's queries before the first page is requested.
+// Pages in each wave's ring: as many as its LDS area holds (at least two,
+// at most four), the area being sized for two pages or for the first group's
+// staged queries, whichever is larger.
+template <int D, bool MX, int RG, int MT>
+constexpr int ring_pages() {
+  constexpr int pb = Geometry<D, MX>::kPageBytes;
+  constexpr int area = 2 * pb > query_stage_bytes<D, RG, MT>() ? 2 * pb : query_stage_bytes<D, RG, MT>();
+  return area / pb > 4 ? 4 : area / pb;
+}
+
+// Each wave's LDS area: its page ring, which also stages the first group's
+// queries before the first page is requested.
 template <int D, bool MX, int RG, int MT>
 union WaveArea {
-  uint8_t page[2][Geometry<D, MX>::kPageBytes];
+  uint8_t page[ring_pages<D, MX, RG, MT>()][Geometry<D, MX>::kPageBytes];
   uint8_t stage[query_stage_bytes<D, RG, MT>() > 0 ? query_stage_bytes<D, RG, MT>() : 16];
 };
 
@@ -380,12 +390,16 @@ __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_
     lds_dma4(src + 1024 * Geo::kWide + 256 * c + 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
 }
 
-// Waits until at most kLoads vector-memory operations are outstanding: every
-// page requested before the most recent one has landed in LDS (vector memory
+// Waits until a page has landed in LDS, given how many pages were requested
+// after it (each page is exactly kLoads requests, and vector memory
 // operations complete in issue order).
 template <int D, bool MX>
-__device__ __forceinline__ void wait_all_but_last_page() {
-  wait_vmcnt<Geometry<D, MX>::kLoads>();
+__device__ __forceinline__ void wait_page_with_later(int later) {
+  constexpr int n = Geometry<D, MX>::kLoads;
+  if (later >= 3) wait_vmcnt<3 * n>();
+  else if (later == 2) wait_vmcnt<2 * n>();
+  else if (later == 1) wait_vmcnt<n>();
+  else wait_all_loads();
 }
 
 // Head weights of the group's rows as the accumulator layout needs them:
@@ -616,7 +630,9 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
 
   float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
   WaveArea<D, MX, RG, MT>& area = sm.area[wave];
-  const uint32_t buf_lds[2] = {lds_addr(area.page[0]), lds_addr(area.page[1])};
+  constexpr int NP = ring_pages<D, MX, RG, MT>();
+  static_assert(NP >= 2 && NP <= 4, "ring of two to four pages");
+  const uint32_t ring_lds = lds_addr(area.page[0]);  // page i of the ring at ring_lds + i * kPageBytes
 
   bool bad_page = false;
   if (j0 < j1) {
@@ -648,12 +664,16 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
     g_first = sm.page_prefix[gs];
     int cur_g = gs;
 
-    const int id0 = id_of(j0);
-    const int id1 = j0 + 1 < j1 ? id_of(j0 + 1) : 0;
+    int first[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) first[i] = j0 + i < j1 ? id_of(j0 + i) : 0;
     wait_all_loads();  // nothing the compiler loaded before is still in flight
     wait_lds();        // the staged query reads have returned: the area is free
-    dma_page<D, MX>(p, id0, buf_lds[0]);
-    if (j0 + 1 < j1) dma_page<D, MX>(p, id1, buf_lds[1]);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if (j0 + i < j1) dma_page<D, MX>(p, first[i], ring_lds + i * Geometry<D, MX>::kPageBytes);
+
+    int slot = 0;  // ring slot of page j
 
     for (int j = j0; j < j1; ++j) {
       gs = advance_group(sm.page_prefix, gs, j);
@@ -664,14 +684,13 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
-      const int nxt = j + 2 < j1 ? id_of(j + 2) : 0;
-      // page j has landed once only the requests after it (page j + 1, if
-      // any) are outstanding
-      if (j + 1 < j1) wait_all_but_last_page<D, MX>();
-      else wait_all_loads();
-      const int slot = (j - j0) & 1;
+      const int nxt = j + NP < j1 ? id_of(j + NP) : 0;
+      // page j has landed once only the requests after it (pages up to
+      // j + NP - 1) are outstanding
+      wait_page_with_later<D, MX>((j + NP - 1 < j1 - 1 ? j + NP - 1 : j1 - 1) - j);
       score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
-      if (j + 2 < j1) dma_page<D, MX>(p, nxt, buf_lds[slot]);  // page j + 2 into the freed buffer
+      if (j + NP < j1) dma_page<D, MX>(p, nxt, ring_lds + slot * Geometry<D, MX>::kPageBytes);  // into the freed slot
+      slot = slot + 1 == NP ? 0 : slot + 1;
     }
   }
   wait_all_loads();  // no request may still be writing LDS when the wave ends
