@@ -488,6 +488,48 @@ __device__ __forceinline__ void page_logits(const v16f (&acc)[2][MT], const floa
   }
 }
 
+// Raw scores of one row (RG = 1) against 32-key tile nt of a raw page.
+template <int D, bool MX, int MT>
+__device__ __forceinline__ void tile_mfma_raw(const uint8_t* buf, int nt, const QFrag<D, 1, MT>& qf, v16f (&acc)[MT],
+                                              float& key_scale) {
+  using Geo = Geometry<D, MX>;
+  const int lane = lane_id();
+  const uint8_t* rowp = buf + (nt * 32 + (lane & 31)) * Geo::kRowBytes;
+  v8bf bfr[Geo::kKSteps];
+  key_fragments<D, MX>(rowp, lane >> 5, bfr);
+  key_scale = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v16f{};
+#pragma unroll
+  for (int s = 0; s < Geo::kKSteps; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[0][mt][s], bfr[s], acc[mt], 0, 0, 0);
+}
+
+// Logits of one 32-key tile from its raw scores; `off` is the byte offset
+// of this lane's key in the row (out of range: nothing stored).
+template <int MT>
+__device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_scale, const WFrag<1, MT>& wf,
+                                            const RowOut& out, int off) {
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) head_sum<1, MT>(acc[mt], wf, 0, mt, ps);
+  finish_key(ps, key_scale, out, (lane_id() >> 5) == 0 ? off : 0x7FFFFFF0);
+}
+
+constexpr int kBlockRows = 8;  // rows per group = waves per workgroup
+constexpr int kRing = 4;       // page buffers per workgroup
+
+template <int D, bool MX>
+struct BlockShared {
+  int page_prefix[kMaxGroups + 1];
+  int req_tab[4][kMaxReqPrefill + 1];
+  float wbuf[kBlockRows][1][kMaxHeads];
+  int misc[16];
+  alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
+  alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
+};
+
 // Scores the 64 keys of the page in LDS for every row of the group and
 // stores logit t = 64 pg + key of each.  The MFMAs of the second 32-key tile
 // are issued before the head sums of the first, so that those VALU sums run
@@ -674,12 +716,26 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       if (j0 + i < j1) dma_page<D, MX>(p, first[i], ring_lds + i * Geometry<D, MX>::kPageBytes);
 
     int slot = 0;  // ring slot of page j
+    // One-row groups pipeline 32-key tiles across pages: a tile's MFMAs are
+    // issued next to the head sums of the tile before it.
+    v16f acc0[MT], acc1[MT];
+    float ks0 = 0.0f, ks1 = 0.0f;
+    int off1 = 0x7FFFFFF0;  // byte offset of the pending tile (none yet)
+    const int key_off = (lane & 31) * 4;
+    if constexpr (RG == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc1[mt] = v16f{};
+    }
 
     for (int j = j0; j < j1; ++j) {
       gs = advance_group(sm.page_prefix, gs, j);
       if (gs != cur_g) {
         // a later group (waiting for its loads drains the page requests in
         // flight; a wave's range crosses few group boundaries)
+        if constexpr (RG == 1) {
+          tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the old group's pending tile
+          off1 = 0x7FFFFFF0;
+        }
         setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out, nullptr);
         g_first = sm.page_prefix[gs];
         cur_g = gs;
@@ -688,10 +744,23 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       // page j has landed once only the requests after it (pages up to
       // j + NP - 1) are outstanding
       wait_page_with_later<D, MX>((j + NP - 1 < j1 - 1 ? j + NP - 1 : j1 - 1) - j);
-      score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
+      if constexpr (RG == 1) {
+        const uint8_t* buf = area.page[slot];
+        const int base = (j - g_first) * kPage * 4 + key_off;
+        tile_mfma_raw<D, MX, MT>(buf, 0, qf, acc0, ks0);
+        tile_logits<MT>(acc1, ks1, wf, out[0], off1);
+        __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
+        tile_mfma_raw<D, MX, MT>(buf, 1, qf, acc1, ks1);
+        tile_logits<MT>(acc0, ks0, wf, out[0], base);
+        __builtin_amdgcn_sched_barrier(0);
+        off1 = base + 32 * 4;
+      } else {
+        score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
+      }
       if (j + NP < j1) dma_page<D, MX>(p, nxt, ring_lds + slot * Geometry<D, MX>::kPageBytes);  // into the freed slot
       slot = slot + 1 == NP ? 0 : slot + 1;
     }
+    if constexpr (RG == 1) tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the last tile
   }
   wait_all_loads();  // no request may still be writing LDS when the wave ends
   if (bad_page && lane == 0) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, kStatusBadPage);
@@ -708,30 +777,6 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
 // in LDS.  Wave 0 requests pages kRing - 1 ahead.  Each page is decoded to
 // bf16 once, by all waves together (an eighth each), into one of two
 // decoded-page buffers, so that the per-row VALU work is the head sums.
-
-// Logits of one 32-key tile from its raw scores; `off` is the byte offset
-// of this lane's key in the row (out of range: nothing stored).
-template <int MT>
-__device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_scale, const WFrag<1, MT>& wf,
-                                            const RowOut& out, int off) {
-  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) head_sum<1, MT>(acc[mt], wf, 0, mt, ps);
-  finish_key(ps, key_scale, out, (lane_id() >> 5) == 0 ? off : 0x7FFFFFF0);
-}
-
-constexpr int kBlockRows = 8;  // rows per group = waves per workgroup
-constexpr int kRing = 4;       // page buffers per workgroup
-
-template <int D, bool MX>
-struct BlockShared {
-  int page_prefix[kMaxGroups + 1];
-  int req_tab[4][kMaxReqPrefill + 1];
-  float wbuf[kBlockRows][1][kMaxHeads];
-  int misc[16];
-  alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
-  alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
-};
 
 // Decodes this wave's share of a raw page into B-fragment order: fragment
 // (tile nt, k-step s) of lane l goes to dec[(nt KS + s) 64 + l], so that a
