@@ -51,7 +51,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PREFILL_KERNEL_SUBSTR = "score_block_kernel<128, false, 2>"
 PREFILL_PROFILE_NAME = "score_block_kernel_fp8_prefill"
 PROFILE_NAME = "score_kernel_fp8_decode_32req"
-KERNEL_SUBSTR = "score_kernel<128, false, 1, 2>"   # scorer: D=128, fp8, 1 row/group, 64 heads
+KERNEL_SUBSTR = "score_kernel<128, false, 2>"   # scorer: D=128, fp8, 64 heads
 TOPK_SUBSTR = "topk_kernel<"
 CALIB_SUBSTR = "AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float>"
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
@@ -277,8 +277,7 @@ def run(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["total"],
-                     "kernel": f"score_kernel<D={wl.head_dim}, {wl.fmt}, {1 if wl.next_n == 1 else 2} row(s)/group, "
-                               f"{wl.heads} heads> (idx_logits_paged)"},
+                     "kernel": f"score_kernel<D={wl.head_dim}, {wl.fmt}, {wl.heads} heads> (idx_logits_paged)"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -113,10 +113,9 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   return IDX_OK;
 }
 
-int pick_rg(const RowArgs& R) {
-  if (R.kind != 0) return kBlockRows;  // prefill: one group of consecutive rows per workgroup
-  return R.next_n == 1 ? 1 : 2;
-}
+// Rows per scorer group: prefill, kBlockRows consecutive query rows per
+// workgroup; decode, one row (a wave's page range walks one row at a time).
+int pick_rg(const RowArgs& R) { return R.kind != 0 ? kBlockRows : 1; }
 
 // Upper bound of the scorer's row groups.
 int64_t group_bound(const RowArgs& R, int rg) {
@@ -137,9 +136,9 @@ size_t decode_ws_bytes(const RowArgs& R) {
   return scratch_offset() + sizeof(float) * static_cast<size_t>(R.num_rows) * scratch_stride(R);
 }
 
-template <int D, bool MX, int RG, int MT>
+template <int D, bool MX, int MT>
 hipError_t launch_score(const ScoreParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((score_kernel<D, MX, RG, MT>), dim3(grid), dim3(score_waves(RG, MT) * kWave), 0, s, p);
+  hipLaunchKernelGGL((score_kernel<D, MX, MT>), dim3(grid), dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
@@ -149,7 +148,7 @@ hipError_t launch_block(const ScoreParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s) {
+hipError_t dispatch_score(const ScoreParams& p, int grid, hipStream_t s) {
   const int d = p.cache.head_dim;
   const bool mx = p.cache.fmt == IDX_FMT_MXFP4;
   const int mt = p.heads > 32 ? 2 : 1;
@@ -163,10 +162,9 @@ hipError_t dispatch_score(const ScoreParams& p, int rg, int grid, hipStream_t s)
 #undef IDX_BLOCK_CASE
     return hipErrorInvalidValue;
   }
-#define IDX_SCORE_CASE(D_, MX_, RG_, MT_) \
-  if (d == D_ && mx == MX_ && rg == RG_ && mt == MT_) return launch_score<D_, MX_, RG_, MT_>(p, grid, s);
-#define IDX_SCORE_RGMT(D_, MX_) \
-  IDX_SCORE_CASE(D_, MX_, 1, 1) IDX_SCORE_CASE(D_, MX_, 1, 2) IDX_SCORE_CASE(D_, MX_, 2, 1) IDX_SCORE_CASE(D_, MX_, 2, 2)
+#define IDX_SCORE_CASE(D_, MX_, MT_) \
+  if (d == D_ && mx == MX_ && mt == MT_) return launch_score<D_, MX_, MT_>(p, grid, s);
+#define IDX_SCORE_RGMT(D_, MX_) IDX_SCORE_CASE(D_, MX_, 1) IDX_SCORE_CASE(D_, MX_, 2)
   IDX_SCORE_RGMT(128, false)
   IDX_SCORE_RGMT(64, false)
   IDX_SCORE_RGMT(32, false)
@@ -272,7 +270,7 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
   p.logits_stride = logits_stride;
   p.header = static_cast<int32_t*>(workspace);
   p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-  const hipError_t e = dispatch_score(p, rg, score_grid(R, rg), static_cast<hipStream_t>(stream));
+  const hipError_t e = dispatch_score(p, score_grid(R, rg), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
 }
 
@@ -323,7 +321,7 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
     p.logits_stride = scratch_stride(R);
     p.header = reinterpret_cast<int32_t*>(ws);
     p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-    if (dispatch_score(p, rg, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
+    if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
   }
   return launch_topk(logits, scratch_stride(R), R, k, out, s);
 }

@@ -4,13 +4,14 @@
 // Two kernels share the helpers below: score_kernel for decode rows and
 // score_block_kernel (at the end of this file) for prefill rows.
 //
-// Work decomposition.  Rows are bundled into "groups" of up to RG rows that
-// share one request (the next_n decode rows of a request, or consecutive
-// query rows of a prefill request); a group reads its request's pages once
-// for all its rows.  Every workgroup (one per CU) builds the prefix of pages
-// over groups in LDS from the device lengths (the host never reads them);
-// the global page list is then cut into equal contiguous ranges, one per
-// wave (decode) or one per workgroup (prefill).
+// Work decomposition.  Rows are bundled into "groups" that share one
+// request: a decode group is one row (the next_n rows of a request are
+// scored by different waves that run at the same time, so a page's second
+// read mostly hits the caches), a prefill group is up to eight consecutive
+// query rows that read the request's pages once.  Every workgroup (one per
+// CU) builds the prefix of pages over groups in LDS from the device lengths
+// (the host never reads them); the global page list is then cut into equal
+// contiguous ranges, one per wave (decode) or one per workgroup (prefill).
 //
 // Decode memory pipeline.  Each wave streams its pages through a ring of NP
 // (2-4) pages in LDS filled by direct global->LDS loads
@@ -46,10 +47,9 @@
 
 namespace idx {
 
-// Waves per workgroup (one workgroup per CU): eight, or four when a wave
-// holds the query fragments of two rows of 64 heads (the register file of a
-// SIMD then holds one such wave).
-constexpr int score_waves(int rg, int mt) { return rg * mt >= 4 ? 4 : 8; }
+// Waves per decode workgroup (one workgroup per CU); every wave scores one
+// row at a time.
+constexpr int kDecodeWaves = 8;
 
 struct ScoreParams {
   CacheArgs cache;
@@ -443,52 +443,7 @@ __device__ __forceinline__ void finish_key(const float (&ps)[4], float key_scale
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out, off, 0, 0);
 }
 
-// Raw scores of one row against the 64 keys of the page in LDS: for each
-// 32-key tile nt, the MT accumulator tiles (heads x keys) and the keys' fp8
-// scales.
-template <int D, bool MX, int RG, int MT>
-__device__ __forceinline__ void page_mfma(const uint8_t* buf, const QFrag<D, RG, MT>& qf, int r, v16f (&acc)[2][MT],
-                                          float (&key_scale)[2]) {
-  using Geo = Geometry<D, MX>;
-  constexpr int KS = Geo::kKSteps;
-  constexpr int RB = Geo::kRowBytes;
-  const int lane = lane_id();
-  const int n = lane & 31;
-  const int g = lane >> 5;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint8_t* rowp = buf + (nt * 32 + n) * RB;
-    v8bf bfr[KS];
-    key_fragments<D, MX>(rowp, g, bfr);
-    key_scale[nt] = MX ? 1.0f : *reinterpret_cast<const float*>(rowp + D);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v16f{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[r][mt][s], bfr[s], acc[nt][mt], 0, 0, 0);
-  }
-}
-
-// Logits of page pg of one row from its raw scores: weighted ReLU head sums,
-// stored at t = 64 pg + key.
-template <int RG, int MT>
-__device__ __forceinline__ void page_logits(const v16f (&acc)[2][MT], const float (&key_scale)[2],
-                                            const WFrag<RG, MT>& wf, int r, const RowOut& out, int pg) {
-  const int lane = lane_id();
-  const int n = lane & 31;
-  const int g = lane >> 5;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) head_sum<RG, MT>(acc[nt][mt], wf, r, mt, ps);
-    finish_key(ps, key_scale[nt], out, g == 0 ? (pg * kPage + nt * 32 + n) * 4 : 0x7FFFFFF0);
-  }
-}
-
-// Raw scores of one row (RG = 1) against 32-key tile nt of a raw page.
+// Raw scores of one row against 32-key tile nt of a raw page in LDS.
 template <int D, bool MX, int MT>
 __device__ __forceinline__ void tile_mfma_raw(const uint8_t* buf, int nt, const QFrag<D, 1, MT>& qf, v16f (&acc)[MT],
                                               float& key_scale) {
@@ -529,22 +484,6 @@ struct BlockShared {
   alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
   alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
 };
-
-// Scores the 64 keys of the page in LDS for every row of the group and
-// stores logit t = 64 pg + key of each.  The MFMAs of the second 32-key tile
-// are issued before the head sums of the first, so that those VALU sums run
-// while the matrix core works.
-template <int D, bool MX, int RG, int MT>
-__device__ __forceinline__ void score_page(const uint8_t* buf, const WFrag<RG, MT>& wf, const QFrag<D, RG, MT>& qf,
-                                           const RowOut (&out)[RG], int pg) {
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    v16f acc[2][MT];
-    float key_scale[2];
-    page_mfma<D, MX, RG, MT>(buf, qf, r, acc, key_scale);
-    page_logits<RG, MT>(acc, key_scale, wf, r, out[r], pg);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // The scorer kernel
@@ -604,75 +543,73 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
   return R.block_table[static_cast<int64_t>(b) * R.bt_stride + (j - page_prefix[g])];
 }
 
-// A group's rows, query fragments, head weights (through the wave's LDS
-// staging row, into the accumulator layout) and output descriptors.
-// `stage` is the wave's idle LDS area for a staged query load, or null.
-template <int D, int RG, int MT>
-__device__ __forceinline__ void setup_group(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
-                                            float (*wbuf)[kMaxHeads], QFrag<D, RG, MT>& qf, WFrag<RG, MT>& wf,
-                                            RowOut (&out)[RG], uint8_t* stage) {
+// The row of group g (decode groups hold one row): its query fragments,
+// head weights (through the wave's LDS staging row, into the accumulator
+// layout) and output descriptor.  `stage` is the wave's idle LDS area for a
+// staged query load, or null.  Returns the row's key count.
+template <int D, int MT>
+__device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
+                                         float* wrow, QFrag<D, 1, MT>& qf, WFrag<1, MT>& wf, RowOut& out,
+                                         uint8_t* stage) {
   const RowArgs& R = p.rows;
   const int lane = lane_id();
-  int L[RG], ql[RG];
-  bool rl[RG];
-  const GroupDesc gd = describe_group<RG>(R, req_tab, g, group_request<RG>(R, req_tab, g), L, ql, rl);
+  int L[1], qr[1];
+  bool rl[1];
+  const GroupDesc gd = describe_group<1>(R, req_tab, g, group_request<1>(R, req_tab, g), L, qr, rl);
+  const int Lr = gd.nrows > 0 ? L[0] : 0;
+  const bool real = rl[0];
   // weights first: they land with (not after) the queries
-  float wv[RG];
-#pragma unroll
-  for (int r = 0; r < RG; ++r) wv[r] = p.w[static_cast<int64_t>(rl[r] ? ql[r] : 0) * p.heads + (lane < p.heads ? lane : 0)];
-  if constexpr (query_stage_bytes<D, RG, MT>() > 0) {
-    if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, RG, MT>(p, ql, stage, qf);
-    else load_query<D, RG, MT>(p, ql, qf);
+  const float wv = p.w[static_cast<int64_t>(real ? qr[0] : 0) * p.heads + (lane < p.heads ? lane : 0)];
+  if constexpr (query_stage_bytes<D, 1, MT>() > 0) {
+    if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, 1, MT>(p, qr, stage, qf);
+    else load_query<D, 1, MT>(p, qr, qf);
   } else {
-    load_query<D, RG, MT>(p, ql, qf);
+    load_query<D, 1, MT>(p, qr, qf);
   }
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    wbuf[r][lane] = (!rl[r] || lane >= p.heads) ? 0.0f : wv[r];
-    out[r] = row_out(p.logits + static_cast<int64_t>(gd.row0 + r) * p.logits_stride + gd.col0,
-                     r < gd.nrows ? L[r] : 0);
-  }
+  wrow[lane] = (!real || lane >= p.heads) ? 0.0f : wv;
+  out = row_out(p.logits + static_cast<int64_t>(gd.row0) * p.logits_stride + gd.col0, Lr);
   __builtin_amdgcn_wave_barrier();
   const int hg = 4 * (lane >> 5);
 #pragma unroll
-  for (int r = 0; r < RG; ++r)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 x = *reinterpret_cast<const float4*>(&wbuf[r][32 * mt + 8 * i4 + hg]);
-        wf.v[r][mt][4 * i4 + 0] = x.x;
-        wf.v[r][mt][4 * i4 + 1] = x.y;
-        wf.v[r][mt][4 * i4 + 2] = x.z;
-        wf.v[r][mt][4 * i4 + 3] = x.w;
-      }
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 x = *reinterpret_cast<const float4*>(&wrow[32 * mt + 8 * i4 + hg]);
+      wf.v[0][mt][4 * i4 + 0] = x.x;
+      wf.v[0][mt][4 * i4 + 1] = x.y;
+      wf.v[0][mt][4 * i4 + 2] = x.z;
+      wf.v[0][mt][4 * i4 + 3] = x.w;
+    }
   __builtin_amdgcn_wave_barrier();
+  return __builtin_amdgcn_readfirstlane(Lr);
 }
 
-template <int D, bool MX, int RG, int MT>
-__global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(ScoreParams p) {
-  constexpr int kScoreWaves = score_waves(RG, MT);
-  constexpr int kScoreThreads = kScoreWaves * kWave;
-  __shared__ ScoreShared<D, MX, RG, MT, kScoreWaves> sm;
+// Decode scorer: every decode row is a group of its own (the next_n rows of
+// a request read the request's pages separately; their waves run at the
+// same time, so the second read mostly hits the caches).
+template <int D, bool MX, int MT>
+__global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScoreParams p) {
+  constexpr int kThreads = kDecodeWaves * kWave;
+  __shared__ ScoreShared<D, MX, 1, MT, kDecodeWaves> sm;
   const RowArgs& R = p.rows;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const bool tables = R.kind != 0 || R.q_packed;
-  const int NG = tables ? build_request_tables<RG, kScoreThreads>(R, sm) : p.num_groups;
+  const int NG = tables ? build_request_tables<1, kThreads>(R, sm) : p.num_groups;
 
-  build_page_prefix<RG, kScoreThreads>(R, sm, NG);
+  build_page_prefix<1, kThreads>(R, sm, NG);
   const int P = sm.page_prefix[NG];
 
   // this wave's contiguous page range
   int j0, j1;
-  even_split(P, gridDim.x * kScoreWaves, blockIdx.x * kScoreWaves + __builtin_amdgcn_readfirstlane(wave), j0, j1);
+  even_split(P, gridDim.x * kDecodeWaves, blockIdx.x * kDecodeWaves + wave, j0, j1);
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
 
-  float(*wbuf)[kMaxHeads] = sm.wbuf[wave];
-  WaveArea<D, MX, RG, MT>& area = sm.area[wave];
-  constexpr int NP = ring_pages<D, MX, RG, MT>();
+  float* wrow = sm.wbuf[wave][0];
+  WaveArea<D, MX, 1, MT>& area = sm.area[wave];
+  constexpr int NP = ring_pages<D, MX, 1, MT>();
   static_assert(NP >= 2 && NP <= 4, "ring of two to four pages");
   const uint32_t ring_lds = lds_addr(area.page[0]);  // page i of the ring at ring_lds + i * kPageBytes
 
@@ -682,11 +619,11 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
     // compiler-visible load sits between page requests; a later batch costs
     // one drain of the requests in flight.
     int jb = j0;
-    int ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+    int ids = page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
     auto id_of = [&](int j) -> int {  // j < j1
       if (j - jb >= kWave) {
         jb = j;
-        ids = page_ids<RG>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+        ids = page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
       }
       const int id = __builtin_amdgcn_readlane(ids, j - jb);
       const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
@@ -697,13 +634,12 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
     // The first group's queries and weights are loaded together with the
     // ids and before any page is requested: waiting for them then never
     // waits for a page, and the first page can be scored as soon as it lands.
-    QFrag<D, RG, MT> qf;
-    WFrag<RG, MT> wf;
-    RowOut out[RG];
+    QFrag<D, 1, MT> qf;
+    WFrag<1, MT> wf;
+    RowOut out;
     int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
-    int g_first = 0;                                  // its first global page
-    setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out, area.stage);
-    g_first = sm.page_prefix[gs];
+    int row_len = setup_row<D, MT>(p, sm.req_tab, gs, wrow, qf, wf, out, area.stage);
+    int g_first = sm.page_prefix[gs];  // the group's first global page
     int cur_g = gs;
 
     int first[NP];
@@ -716,27 +652,23 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       if (j0 + i < j1) dma_page<D, MX>(p, first[i], ring_lds + i * Geometry<D, MX>::kPageBytes);
 
     int slot = 0;  // ring slot of page j
-    // One-row groups pipeline 32-key tiles across pages: a tile's MFMAs are
-    // issued next to the head sums of the tile before it.
+    // 32-key tiles are pipelined across pages: a tile's MFMAs are issued
+    // next to the head sums of the tile before it.
     v16f acc0[MT], acc1[MT];
     float ks0 = 0.0f, ks1 = 0.0f;
     int off1 = 0x7FFFFFF0;  // byte offset of the pending tile (none yet)
     const int key_off = (lane & 31) * 4;
-    if constexpr (RG == 1) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc1[mt] = v16f{};
-    }
+    for (int mt = 0; mt < MT; ++mt) acc1[mt] = v16f{};
 
     for (int j = j0; j < j1; ++j) {
       gs = advance_group(sm.page_prefix, gs, j);
       if (gs != cur_g) {
         // a later group (waiting for its loads drains the page requests in
         // flight; a wave's range crosses few group boundaries)
-        if constexpr (RG == 1) {
-          tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the old group's pending tile
-          off1 = 0x7FFFFFF0;
-        }
-        setup_group<D, RG, MT>(p, sm.req_tab, gs, wbuf, qf, wf, out, nullptr);
+        tile_logits<MT>(acc1, ks1, wf, out, off1);  // the old group's pending tile
+        off1 = 0x7FFFFFF0;
+        row_len = setup_row<D, MT>(p, sm.req_tab, gs, wrow, qf, wf, out, nullptr);
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
@@ -744,23 +676,21 @@ __global__ __launch_bounds__(score_waves(RG, MT) * kWave, 1) void score_kernel(S
       // page j has landed once only the requests after it (pages up to
       // j + NP - 1) are outstanding
       wait_page_with_later<D, MX>((j + NP - 1 < j1 - 1 ? j + NP - 1 : j1 - 1) - j);
-      if constexpr (RG == 1) {
+      if (row_len > 0) {  // wave-uniform: a padded slot only keeps the ring moving
         const uint8_t* buf = area.page[slot];
         const int base = (j - g_first) * kPage * 4 + key_off;
         tile_mfma_raw<D, MX, MT>(buf, 0, qf, acc0, ks0);
-        tile_logits<MT>(acc1, ks1, wf, out[0], off1);
+        tile_logits<MT>(acc1, ks1, wf, out, off1);
         __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
         tile_mfma_raw<D, MX, MT>(buf, 1, qf, acc1, ks1);
-        tile_logits<MT>(acc0, ks0, wf, out[0], base);
+        tile_logits<MT>(acc0, ks0, wf, out, base);
         __builtin_amdgcn_sched_barrier(0);
         off1 = base + 32 * 4;
-      } else {
-        score_page<D, MX, RG, MT>(area.page[slot], wf, qf, out, j - g_first);
       }
       if (j + NP < j1) dma_page<D, MX>(p, nxt, ring_lds + slot * Geometry<D, MX>::kPageBytes);  // into the freed slot
       slot = slot + 1 == NP ? 0 : slot + 1;
     }
-    if constexpr (RG == 1) tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the last tile
+    tile_logits<MT>(acc1, ks1, wf, out, off1);  // the last tile
   }
   wait_all_loads();  // no request may still be writing LDS when the wave ends
   if (bad_page && lane == 0) atomicOr(reinterpret_cast<uint32_t*>(p.header) + kHdrStatus, kStatusBadPage);

@@ -37,6 +37,10 @@ SHAPES = [
     ("mxfp4", 128, 64, 1, False),
     ("mxfp4", 128, 64, 2, False),
     ("mxfp4", 128, 8, 1, False),
+    ("fp8", 128, 64, 4, False),
+    ("fp8", 128, 64, 3, True),
+    ("fp8", 64, 16, 5, False),
+    ("mxfp4", 128, 64, 4, True),
 ]
 
 
