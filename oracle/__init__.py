@@ -10,7 +10,8 @@ to be read against its sources:
   per-token decode lengths, the prefill chunk planner and chunk windows;
 * the vLLM glm5next ``sparse_indexer`` helper page: padded non-uniform decode
   grids, causal fill, the MXFP4 cache row width;
-* the vLLM MiniMax-M3 AMD mono runner page: ``token_rows``.
+* the vLLM MiniMax-M3 AMD mono runner page: ``token_rows`` and the int64
+  page slots of its caches (the cache write, ``cache_write``).
 
 The score itself, ``logit[t] = scale_t * sum_h w_h * relu(q_h . k_t)``, the
 lower-index tie rule and the exact causal fill when a row's length is at most
@@ -23,4 +24,4 @@ rationals, hand-worked examples, the pages' own worked example); see the
 module docstrings for which pin covers what.
 """
 
-from . import formats, rows, cache, score, topk, planner, pipeline  # noqa: F401
+from . import formats, rows, cache, cache_write, score, topk, planner, pipeline  # noqa: F401
