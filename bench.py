@@ -106,18 +106,22 @@ def scored_keys(wl) -> int:
     return total
 
 
+def _oracle_cores() -> int:
+    """Threads the oracle's numpy (BLAS) uses on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
     """The oracle (numpy, float64) on the host cores: whole requests of the
     batch in order, cycling over the batch, until about `budget_s` seconds
     of work are done."""
-    import numpy as np
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _oracle_cores()
     keys = 0
     t0 = time.perf_counter()
     done = 0
@@ -128,7 +132,7 @@ def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
         keys += int(sum(len(v) for v in lg.values() if len(v) > wl.topk))
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": keys / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+    return {"value": keys / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} requests of the {wl.num_req}-request batch in order, cycling "
                       f"({done / wl.num_req:.1f} passes, {keys} keys, {dt:.1f} s): dequantise, fp64 logits, "
                       f"top-k; cpus visible {len(os.sched_getaffinity(0))}"}
@@ -370,6 +374,74 @@ def run_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def run_cache_write(args):
+    """The index-cache write: 64 x 131072 = 8,388,608 new bf16 key tokens
+    quantised into a pool of exactly that many slots (pages in random order,
+    tokens in order within a page), fp8 and MXFP4, one launch each; a
+    separate line per format."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_decode_amd as idx
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    T, D = 64 * 131072, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    k = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+    # 64 requests of 131072 tokens: each request's pages dealt from one
+    # random permutation of the pool, tokens in order within a page
+    pages = torch.randperm(T // 64, generator=g, device=dev)
+    t = torch.arange(T, device=dev)
+    slots = pages[t // 64] * 64 + t % 64
+    ws = idx.new_workspace(256, dev)
+    stream = torch.cuda.current_stream()
+    for fmt in ("fp8", "mxfp4"):
+        rb = D + 4 if fmt == "fp8" else D // 2 + D // 32
+        page_bytes = (64 * rb + 15) // 16 * 16
+        pool = torch.zeros((T // 64, page_bytes), dtype=torch.uint8, device=dev)
+        cache = idx.Cache(pool, D, fmt)
+        for _ in range(args.warmup):
+            idx.idx_cache_write(cache, k, slots, ws, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            idx.idx_cache_write(cache, k, slots, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        alg = T * (2 * D + rb + 8)          # bf16 key read, row written, int64 slot read
+        gbs = alg / (ms * 1e-3) / 1e9
+        res = {
+            "metric": "index-cache write: key tokens quantised and stored per second, 1xMI355X",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"cache write: {T} bf16 key tokens, head_dim {D}, {fmt} rows of {rb} B, "
+                                   "int64 slots of 64-token pages dealt at random from a pool of exactly that many slots",
+                       "fmt": fmt, "tokens": T},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg,
+                         "kernel": f"cache_write_kernel<D={D}, {fmt}> (idx_cache_write)"},
+        }
+        if not args.no_cpu_baseline:
+            import oracle
+            sample = 32768
+            kb = k[:sample].view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            n = 0
+            while time.perf_counter() - t0 < args.cpu_budget / 4:
+                oracle.cache_write.quantize_rows(kb, fmt)
+                n += sample
+            dt = time.perf_counter() - t0
+            res["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": _oracle_cores(), "kind": "oracle",
+                                   "sample": f"the first {sample} tokens quantised repeatedly ({n} tokens, {dt:.1f} s)"}
+        print(json.dumps(res), flush=True)
+        del pool
+
+
 def summarize_prefill(stats_dir, pmc_dir, commands, bench_json):
     """Kernel time and SQ counters of the prefill scorer ->
     profiles/score_block_kernel_fp8_prefill.md"""
@@ -525,6 +597,7 @@ def main():
     ap.add_argument("--bench-json", default=None)
     ap.add_argument("--prefill", action="store_true", help="measure the prefill path instead (separate line)")
     ap.add_argument("--summarize-prefill", nargs=2, metavar=("STATS_DIR", "PMC_DIR"))
+    ap.add_argument("--cache-write", action="store_true", help="measure the index-cache write instead (separate lines)")
     args = ap.parse_args()
     if args.summarize_prof:
         summarize(args.summarize_prof, args.commands, args.bench_json)
@@ -538,6 +611,9 @@ def main():
         sys.exit(2)
     if args.prefill:
         run_prefill(args)
+        return
+    if args.cache_write:
+        run_cache_write(args)
         return
     run(args)
 

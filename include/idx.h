@@ -62,6 +62,7 @@ typedef int32_t idx_status;
 
 /* Bits of the device status word (first 4 bytes of a workspace). */
 #define IDX_DEV_BAD_PAGE 1u
+#define IDX_DEV_BAD_SLOT 2u  /* idx_cache_write: a slot at or past num_pages * 64 */
 
 /*
  * Paged index cache (the `(num_blocks, block_size, head_size)` allocation of
@@ -144,6 +145,7 @@ int64_t idx_num_rows(const idx_rows* rows);
 #define IDX_OP_LOGITS 0
 #define IDX_OP_TOPK 1
 #define IDX_OP_DECODE_TOPK 2
+#define IDX_OP_CACHE_WRITE 3
 
 /*
  * Bytes of device workspace `op` needs for these arguments (the caller
@@ -155,6 +157,7 @@ int64_t idx_num_rows(const idx_rows* rows);
  */
 size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* rows,
                            int32_t heads, int32_t k);
+/* (IDX_OP_CACHE_WRITE needs only `cache`; rows may be NULL.) */
 
 /*
  * Logits of every row (the scorer the DeepSeek-V3.2 page calls
@@ -199,6 +202,40 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
                            const float* w, int32_t heads, int32_t k, int32_t* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Index-cache write: quantise new key tokens and store each token's row in
+ * the paged cache at its slot, the step that fills the cache the scorer
+ * reads.  The int64 per-token slot mapping is the one the DeepSeek-V3.2
+ * indexer page's metadata carries (slot_mapping and its compressed variant)
+ * and the MiniMax-M3 mono runner page documents for its page slots: token t
+ * goes to row slot % 64 of page slot / 64; a negative slot (a padding token)
+ * is skipped.  The row layouts are those of idx_cache (the glm5next page's
+ * _gather_workspace_shapes).  The pages do not print the quantiser; this one
+ * follows the per-token absmax / OCP MX block-scale reading:
+ *   FP8_E4M3  scale = amax/448 as an fp32 division (1 for an all-zero row),
+ *             code_d = e4m3fn(k_d / scale): fp32 division, clamped to +-448,
+ *             round to nearest even.
+ *   MXFP4     per 32-element block e = floor(log2 amax) - 2, at least -127
+ *             (an all-zero block gets -127), ue8m0 byte e + 127, elements
+ *             k_d * 2^-e rounded to the nearest e2m1 value (ties to the even
+ *             code), saturating at +-6.
+ *   Every code keeps the key's sign bit.
+ * Arguments:
+ *   cache         its base must be writable device memory
+ *   k             device bf16 bits [num_tokens, k_stride], the first head_dim
+ *                 elements of each row used; 16-byte aligned, k_stride a
+ *                 multiple of 8 and >= head_dim
+ *   slot_mapping  device int64 [num_tokens], 8-byte aligned; slots must be
+ *                 distinct (two tokens on one slot race)
+ *   num_tokens    >= 0 (0 enqueues nothing)
+ * A slot at or past num_pages * 64 is skipped and sets IDX_DEV_BAD_SLOT in
+ * the workspace status word.  Workspace: idx_workspace_bytes(
+ * IDX_OP_CACHE_WRITE, cache, NULL, 0, 0) bytes (the status word only).
+ */
+idx_status idx_cache_write(const idx_cache* cache, const uint16_t* k, int64_t k_stride,
+                           const int64_t* slot_mapping, int64_t num_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Host-only prefill planner (split_indexer_prefill_chunks and

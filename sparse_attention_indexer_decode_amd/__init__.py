@@ -10,10 +10,13 @@ from .binding import (  # noqa: F401
     IdxError,
     Rows,
     EXPORTED,
+    IDX_OP_CACHE_WRITE,
     IDX_OP_DECODE_TOPK,
     IDX_OP_LOGITS,
     IDX_OP_TOPK,
     IDX_DEV_BAD_PAGE,
+    IDX_DEV_BAD_SLOT,
+    idx_cache_write,
     idx_decode_topk,
     idx_logits_paged,
     idx_prefill_chunks,

@@ -20,8 +20,8 @@ from ._build import LIB_PATH
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_ENOSPC, IDX_EHIP = 0, 1, 2, 3, 4
 IDX_FMT_FP8_E4M3, IDX_FMT_MXFP4 = 0, 1
 IDX_ROWS_DECODE, IDX_ROWS_PREFILL = 0, 1
-IDX_OP_LOGITS, IDX_OP_TOPK, IDX_OP_DECODE_TOPK = 0, 1, 2
-IDX_DEV_BAD_PAGE = 1
+IDX_OP_LOGITS, IDX_OP_TOPK, IDX_OP_DECODE_TOPK, IDX_OP_CACHE_WRITE = 0, 1, 2, 3
+IDX_DEV_BAD_PAGE, IDX_DEV_BAD_SLOT = 1, 2
 
 FMT_CODES = {"fp8": IDX_FMT_FP8_E4M3, "mxfp4": IDX_FMT_MXFP4}
 
@@ -31,6 +31,7 @@ EXPORTED = (
     "idx_logits_paged",
     "idx_topk",
     "idx_decode_topk",
+    "idx_cache_write",
     "idx_prefill_chunks",
     "idx_read_device_status",
     "idx_status_string",
@@ -90,6 +91,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.idx_decode_topk.argtypes = [POINTER(IdxCache), POINTER(IdxRows), c_void_p, c_void_p, c_int32,
                                     c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.idx_decode_topk.restype = c_int32
+    lib.idx_cache_write.argtypes = [POINTER(IdxCache), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t,
+                                    c_void_p]
+    lib.idx_cache_write.restype = c_int32
     lib.idx_prefill_chunks.argtypes = [POINTER(c_int32), POINTER(c_int32), c_int32, c_int64, c_int64,
                                        c_int32, POINTER(IdxChunk), c_int32, POINTER(c_int32)]
     lib.idx_prefill_chunks.restype = c_int32
@@ -178,9 +182,9 @@ class Rows:
 # Entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
 
-def idx_workspace_bytes(op: int, cache: Cache | None, rows: Rows, heads: int, k: int) -> int:
+def idx_workspace_bytes(op: int, cache: Cache | None, rows: Rows | None, heads: int, k: int) -> int:
     return int(load().idx_workspace_bytes(op, ctypes.byref(cache.c) if cache else None,
-                                          ctypes.byref(rows.c), heads, k))
+                                          ctypes.byref(rows.c) if rows else None, heads, k))
 
 
 def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -214,6 +218,18 @@ def idx_decode_topk(cache: Cache, rows: Rows, q: torch.Tensor, w: torch.Tensor, 
     _check("idx_decode_topk", load().idx_decode_topk(
         ctypes.byref(cache.c), ctypes.byref(rows.c), q.data_ptr(), w.data_ptr(), q.shape[1], k,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def idx_cache_write(cache: Cache, k: torch.Tensor, slot_mapping: torch.Tensor, workspace: torch.Tensor,
+                    stream=None) -> None:
+    """k: bf16 [num_tokens, >= head_dim] (unit element stride); slot_mapping:
+    int64 [num_tokens]."""
+    assert k.dtype == torch.bfloat16 and k.dim() == 2 and k.stride(1) == 1
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    assert slot_mapping.shape[0] == k.shape[0]
+    _check("idx_cache_write", load().idx_cache_write(
+        ctypes.byref(cache.c), k.data_ptr(), _row_stride(k), slot_mapping.data_ptr(), k.shape[0],
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def idx_prefill_chunks(seq_lens, query_lens, workspace_tokens: int, max_logits_bytes: int,

@@ -15,6 +15,7 @@ constexpr int kStatusBytes = 256;  // workspace header: status word + pad
 // Workspace header layout (int32 slots).
 constexpr int kHdrStatus = 0;
 constexpr uint32_t kStatusBadPage = 1u;  // a block-table entry outside the pool (IDX_DEV_BAD_PAGE)
+constexpr uint32_t kStatusBadSlot = 2u;  // a cache-write slot past the pool (IDX_DEV_BAD_SLOT)
 
 struct CacheArgs {
   const uint8_t* base;

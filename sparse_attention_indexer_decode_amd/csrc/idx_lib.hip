@@ -7,6 +7,7 @@
 
 #include "../../include/idx.h"
 #include "idx_internal.h"
+#include "cache_write.cuh"
 #include "score.cuh"
 #include "topk.cuh"
 
@@ -230,6 +231,10 @@ int64_t idx_num_rows(const idx_rows* rows) { return rows_count(rows); }
 size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* rows, int32_t heads,
                            int32_t k) {
   RowArgs R;
+  if (op == IDX_OP_CACHE_WRITE) {
+    CacheArgs C;
+    return check_cache(cache, C) == IDX_OK ? kStatusBytes : 0;
+  }
   if (op == IDX_OP_TOPK) {
     if (check_rows(rows, false, R) != IDX_OK) return 0;
     return kStatusBytes;
@@ -272,6 +277,40 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
   p.num_groups = static_cast<int32_t>(group_bound(R, rg));
   const hipError_t e = dispatch_score(p, score_grid(R, rg), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+}
+
+idx_status idx_cache_write(const idx_cache* cache, const uint16_t* k, int64_t k_stride,
+                           const int64_t* slot_mapping, int64_t num_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  CacheArgs C;
+  idx_status st = check_cache(cache, C);
+  if (st != IDX_OK) return st;
+  if (!k || !slot_mapping) return fail(IDX_EINVAL, "k or slot_mapping is null");
+  if ((reinterpret_cast<uintptr_t>(k) & 15) != 0) return fail(IDX_EINVAL, "k must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7) != 0) return fail(IDX_EINVAL, "slot_mapping must be 8-byte aligned");
+  if (k_stride < C.head_dim || (k_stride & 7) != 0) return fail(IDX_EINVAL, "k_stride must be >= head_dim and a multiple of 8");
+  if (num_tokens < 0) return fail(IDX_EINVAL, "num_tokens < 0");
+  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
+  if (num_tokens == 0) return IDX_OK;
+  CacheWriteParams p{};
+  p.base = const_cast<uint8_t*>(C.base);
+  p.num_pages = C.num_pages;
+  p.page_bytes = C.page_bytes;
+  p.k = k;
+  p.k_stride = k_stride;
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.header = static_cast<int32_t*>(workspace);
+  const int64_t per_block = (kWriteThreads / kWave) * kWriteGroups * (kWave / (C.head_dim / 8));  // tokens per workgroup
+  const int64_t grid = ceil_div(num_tokens, per_block);
+  if (grid > 0x7FFFFFFF) return fail(IDX_EUNSUPPORTED, "num_tokens too large for one launch");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool mx = C.fmt == IDX_FMT_MXFP4;
+  if (mx) hipLaunchKernelGGL((cache_write_kernel<128, true>), dim3(grid), dim3(kWriteThreads), 0, s, p);
+  else if (C.head_dim == 128) hipLaunchKernelGGL((cache_write_kernel<128, false>), dim3(grid), dim3(kWriteThreads), 0, s, p);
+  else if (C.head_dim == 64) hipLaunchKernelGGL((cache_write_kernel<64, false>), dim3(grid), dim3(kWriteThreads), 0, s, p);
+  else hipLaunchKernelGGL((cache_write_kernel<32, false>), dim3(grid), dim3(kWriteThreads), 0, s, p);
+  return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
 }
 
 idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, int32_t k,

@@ -179,3 +179,27 @@ def test_workspace_sizes(lib):
     assert lib.idx_num_rows(ctypes.byref(_rows(num_req=3, next_n=2))) == 6
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=9))) == 5
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=3))) == -1
+
+
+def test_cache_write_validation_and_workspace(lib):
+    E, U, S = B.IDX_EINVAL, B.IDX_EUNSUPPORTED, B.IDX_ENOSPC
+    c = _cache()
+    assert lib.idx_workspace_bytes(B.IDX_OP_CACHE_WRITE, ctypes.byref(c), None, 0, 0) == 256
+    assert lib.idx_workspace_bytes(B.IDX_OP_CACHE_WRITE, ctypes.byref(_cache(head_dim=96)), None, 0, 0) == 0
+
+    def w(cache=None, k=FAKE, stride=128, slots=FAKE, n=10, ws=FAKE, wsb=256):
+        cache = cache or _cache()
+        return lib.idx_cache_write(ctypes.byref(cache), k, stride, slots, n, ws, wsb, None)
+
+    assert lib.idx_cache_write(None, FAKE, 128, FAKE, 10, FAKE, 256, None) == E
+    assert w(cache=_cache(head_dim=96)) == U
+    assert w(k=None) == E
+    assert w(slots=None) == E
+    assert w(k=FAKE + 8) == E                  # k not 16-byte aligned
+    assert w(slots=FAKE + 4) == E              # slots not 8-byte aligned
+    assert w(stride=64) == E                   # < head_dim
+    assert w(stride=132) == E                  # not a multiple of 8
+    assert w(n=-1) == E
+    assert w(wsb=16) == S
+    assert w(ws=FAKE + 8) == E
+    assert w(n=0) == B.IDX_OK                  # nothing to enqueue

@@ -340,3 +340,71 @@ def config(name: str) -> Workload:
                              heads=64, head_dim=128, topk=2048, fmt="fp8", w_std=1.0 / 8,
                              name="C5")
     raise KeyError(name)
+
+
+# ----------------------------------------------------------------------------
+# Cache-write inputs
+# ----------------------------------------------------------------------------
+
+@dataclass
+class CacheWriteInputs:
+    fmt: str
+    head_dim: int
+    k_bits: np.ndarray        # uint16 bf16 [T, k_stride] (first head_dim used)
+    slots: np.ndarray         # int64 [T]
+    num_pages: int
+    page_bytes: int
+    cache: np.ndarray         # uint8 [num_pages, page_bytes], the cache before the write
+
+
+def cache_write_inputs(*, seed: int, tokens: int, head_dim: int, fmt: str, num_pages: int,
+                       k_stride: int | None = None, skip_frac: float = 0.05,
+                       special_rows: bool = True) -> CacheWriteInputs:
+    """New key tokens for an index-cache write: bf16 keys N(0,1) times a
+    per-token power of two in [2^-20, 2^20], distinct random slots of the
+    pool (a fraction set to -1, i.e. not stored) and a poisoned pool.  With
+    `special_rows`, the first rows are edge cases: all zeros, signed zeros,
+    a lone value, constant rows, values exactly halfway between fp8 / fp4
+    codes after scaling, and bf16 subnormals next to a large absmax."""
+    rng = np.random.default_rng(seed)
+    D = head_dim
+    stride = k_stride or D
+    k = rng.standard_normal((tokens, D)).astype(np.float32) * np.exp2(rng.integers(-20, 21, (tokens, 1)))
+    if special_rows:
+        e4m3_ties = np.array([1.0625, 1.1875, 2.125, 3.25, 0.0029296875, 0.0087890625, 14.5, 416.0,
+                              -1.0625, -2.125, -0.0029296875, -416.0], dtype=np.float32)   # halfway between codes
+        fp4_ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -0.75, -2.5, -5.0], dtype=np.float32)
+        specials = []
+        specials.append(np.zeros(D, np.float32))
+        z = np.zeros(D, np.float32)
+        z[1::2] = -0.0
+        specials.append(z)
+        lone = np.zeros(D, np.float32)
+        lone[D // 2] = -3.0
+        specials.append(lone)
+        specials.append(np.full(D, 2.0, np.float32))
+        row = np.zeros(D, np.float32)
+        row[0] = 448.0                                  # fp8 scale exactly 1
+        row[1 : 1 + len(e4m3_ties)] = e4m3_ties
+        specials.append(row)
+        row = np.zeros(D, np.float32)
+        for b in range(D // 32):                        # every block: amax 7 -> block exponent 0
+            row[32 * b] = 7.0
+            row[32 * b + 1 : 32 * b + 1 + len(fp4_ties)] = fp4_ties
+        specials.append(row)
+        row = np.zeros(D, np.float32)
+        row[0] = 1024.0
+        row[1:5] = [2.0 ** -133, -(2.0 ** -133), 2.0 ** -126, -(2.0 ** -130)]
+        specials.append(row)
+        n = min(len(specials), tokens)
+        k[:n] = np.stack(specials[:n])
+    bits = np.zeros((tokens, stride), dtype=np.uint16)
+    bits[:, :D] = _bf16_bits(k)
+    rb = row_bytes_for(fmt, D)
+    page_bytes = (PAGE_SIZE * rb + 15) // 16 * 16
+    cap = num_pages * PAGE_SIZE
+    assert tokens <= cap
+    slots = rng.permutation(cap)[:tokens].astype(np.int64)
+    slots[rng.random(tokens) < skip_frac] = -1
+    cache = np.full((num_pages, page_bytes), 0x5A, dtype=np.uint8)
+    return CacheWriteInputs(fmt, D, bits, slots, num_pages, page_bytes, cache)
