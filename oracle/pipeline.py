@@ -15,7 +15,7 @@ from . import cache, rows, score, topk
 
 def decode_row_info(wl):
     """(L per grid row, q/w row per grid row or -1)."""
-    L = rows.decode_lengths(wl.seq_lens, wl.decode_lens, wl.next_n)
+    L = rows.decode_lengths(wl.seq_lens, wl.decode_lens, wl.next_n, getattr(wl, "compress_ratio", 1))
     qrow = rows.decode_query_rows(wl.decode_lens, wl.next_n, wl.num_req, wl.q_packed)
     return L, qrow
 
@@ -54,7 +54,8 @@ def decode_topk(wl, logits_by_row=None, requests=None):
 def prefill_chunk_row_info(wl, rec):
     """Rows of one chunk record: (request, j, L, ks, q/w row)."""
     req, j, L, ks = rows.prefill_rows(wl.seq_lens, wl.query_lens, rec["req_begin"],
-                                      rec["req_end"], rec["q_begin"], rec["q_end"])
+                                      rec["req_end"], rec["q_begin"], rec["q_end"],
+                                      getattr(wl, "compress_ratio", 1))
     qstart = np.concatenate([[0], np.cumsum(np.asarray(wl.query_lens, dtype=np.int64))])
     qrow = qstart[req] + j
     return req, j, L, ks, qrow
@@ -70,6 +71,6 @@ def prefill_chunk_logits(wl, rec, sample_rows=None):
     for r in idx:
         b = int(req[r])
         if b not in key_cache:
-            key_cache = {b: cache.keys(wl, b, int(wl.seq_lens[b]))}
+            key_cache = {b: cache.keys(wl, b, int(wl.seq_lens[b]) // getattr(wl, "compress_ratio", 1))}
         out[r] = score.logits(wl.q[qrow[r]], wl.w[qrow[r]], key_cache[b][: L[r]])
     return out

@@ -33,6 +33,15 @@ last ones of its ``seq_lens[b]`` keys; its query token ``j`` sees
 on the DeepSeek-V3.2 page, compress ratio 1), stored in the chunk's logits
 columns starting at ``ks = sum(seq_lens[:b])`` (its ``cu_seqlen_ks``).
 
+Compressed index cache (the DeepSeek-V4 variant of the DeepSeek-V3.2
+indexer page: compress_ratio > 1, pages of 256 compressed tokens).  The
+cache stores seq_len // ratio keys per request, and every per-token length
+above is divided by the ratio and rounded down: the page divides the decode
+per-token lengths by the ratio (``seq_lens //= compress_ratio``) and its
+prefill chunk kernel gives token ``offset`` the length
+``(start_pos + 1 + offset) // COMPRESS_RATIO`` with ``start_pos = seq_len -
+query_len``, its columns starting at the compressed prefix sum.
+
 Pins: tests/test_oracle_rows.py (the pages' worked example
 seq [10,7,12,0] / decode [3,1,4,0] -> [8,9,10,7,9,10,11,12]; ``token_rows``;
 brute-force enumeration of the packed mapping).
@@ -43,8 +52,9 @@ from __future__ import annotations
 import numpy as np
 
 
-def decode_lengths(seq_lens, decode_lens, next_n: int) -> np.ndarray:
-    """Per grid row key counts, shape [B * next_n], int64."""
+def decode_lengths(seq_lens, decode_lens, next_n: int, compress_ratio: int = 1) -> np.ndarray:
+    """Per grid row key counts, shape [B * next_n], int64 (with a compressed
+    index cache, the token's length divided by the ratio, rounded down)."""
     seq = np.asarray(seq_lens, dtype=np.int64)
     B = seq.shape[0]
     dl = np.full(B, next_n, dtype=np.int64) if decode_lens is None else np.asarray(decode_lens, dtype=np.int64)
@@ -52,7 +62,7 @@ def decode_lengths(seq_lens, decode_lens, next_n: int) -> np.ndarray:
     for b in range(B):
         for i in range(next_n):
             if i < dl[b]:
-                out[b * next_n + i] = max(0, int(seq[b] - dl[b] + i + 1))
+                out[b * next_n + i] = max(0, int(seq[b] - dl[b] + i + 1)) // compress_ratio
     return out
 
 
@@ -88,13 +98,16 @@ def token_rows(seq_lens, q: int) -> np.ndarray:
     return np.asarray([int(s) - (q - 1 - j) for s in seq for j in range(q)], dtype=np.int64)
 
 
-def prefill_rows(seq_lens, query_lens, req_begin: int, req_end: int, q_begin: int, q_end: int):
+def prefill_rows(seq_lens, query_lens, req_begin: int, req_end: int, q_begin: int, q_end: int,
+                 compress_ratio: int = 1):
     """Rows of one prefill chunk.
 
     The chunk covers requests [req_begin, req_end) and, of their concatenated
     query tokens, the slice [q_begin, q_end).  Returns, per output row in
     order, (request index, query index j within that request, key count L,
-    logits column base ks) as int64 arrays.
+    logits column base ks) as int64 arrays.  With a compressed index cache
+    (ratio r) the key count is (seq_len - query_len + j + 1) // r and ks sums
+    the earlier requests' compressed lengths seq_len // r.
     """
     seq = np.asarray(seq_lens, dtype=np.int64)
     ql = np.asarray(query_lens, dtype=np.int64)
@@ -106,9 +119,9 @@ def prefill_rows(seq_lens, query_lens, req_begin: int, req_end: int, q_begin: in
             if q_begin <= tok < q_end:
                 reqs.append(b)
                 js.append(j)
-                Ls.append(max(0, int(seq[b] - ql[b] + j + 1)))
+                Ls.append(max(0, int(seq[b] - ql[b] + j + 1)) // compress_ratio)
                 kss.append(ks)
             tok += 1
-        ks += int(seq[b])
+        ks += int(seq[b]) // compress_ratio
     return (np.asarray(reqs, dtype=np.int64), np.asarray(js, dtype=np.int64),
             np.asarray(Ls, dtype=np.int64), np.asarray(kss, dtype=np.int64))

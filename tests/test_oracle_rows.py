@@ -63,3 +63,37 @@ def test_prefill_rows_windows():
     assert ks.tolist() == [0, 0, 0, 6, 6]
     req, j, L, ks = rows.prefill_rows(seq, ql, 0, 2, 2, 4)
     assert req.tolist() == [0, 1] and L.tolist() == [6, 3] and ks.tolist() == [0, 6]
+
+
+def test_compressed_lengths_hand_example():
+    """The compressed index cache's lengths: the pages' division rules
+    applied by hand (tests/golden/compressed_lengths.json)."""
+    g = load_golden("compressed_lengths.json")
+    r = g["compress_ratio"]
+    d = g["decode"]
+    L = rows.decode_lengths(d["seq_lens"], d["decode_lens"], d["next_n"], r)
+    assert list(L) == d["grid_lengths"]
+    p = g["prefill"]
+    req, j, L, ks = rows.prefill_rows(p["seq_lens"], p["query_lens"], 0, 2, 0, 8, r)
+    assert list(L) == p["lengths"] and list(ks) == p["ks"]
+    # ratio 1 is the uncompressed rule
+    assert list(rows.decode_lengths(d["seq_lens"], d["decode_lens"], d["next_n"], 1)) == \
+        list(rows.decode_lengths(d["seq_lens"], d["decode_lens"], d["next_n"]))
+
+
+def test_compressed_lengths_brute_force():
+    """Every compressed length equals the count of stored keys at or before
+    the token: key c stands for tokens [c r, c r + r), so it is visible to a
+    token at position p once c r + r <= p + 1."""
+    rng = np.random.default_rng(2)
+    for r in (2, 4, 128):
+        seq = rng.integers(0, 700, 20)
+        dl = np.minimum(rng.integers(0, 4, 20), seq)
+        L = rows.decode_lengths(seq, dl, 3, r)
+        for b in range(20):
+            for i in range(3):
+                if i >= dl[b]:
+                    assert L[b * 3 + i] == 0
+                    continue
+                pos = int(seq[b] - dl[b] + i)
+                assert L[b * 3 + i] == sum(1 for c in range(int(seq[b]) // r) if c * r + r <= pos + 1)

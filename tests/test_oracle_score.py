@@ -145,3 +145,21 @@ def test_cache_read_back_matches_generated_keys():
                 step = np.repeat(np.exp2(e), 32, axis=1)     # half the largest e2m1 gap is 1 * 2^e
                 bound = step * 1.0001 + np.maximum(np.abs(orig) - 6 * step, 0)
             assert np.all(np.abs(got - orig) <= bound), (fmt, b)
+
+
+def test_page256_cache_reads_same_keys_as_page64():
+    """Keys are drawn in token order whatever the page size, so a workload
+    stored in 256-token pages and one in 64-token pages (same seed) hold the
+    same keys; the oracle's block-table reader must return them equally."""
+    from oracle import cache
+    from workloads import build_decode
+    kw = dict(seed=31, seq_lens=[1, 255, 256, 257, 700], heads=4, head_dim=64, topk=16)
+    # explicit tables (request r owns a run of pages, in reverse order) so that
+    # both draw their keys from the same generator state
+    bt64 = np.array([[r * 11 + 10 - i for i in range(11)] for r in range(5)], dtype=np.int32)
+    bt256 = np.array([[r * 3 + 2 - i for i in range(3)] for r in range(5)], dtype=np.int32)
+    a = build_decode(**kw, block_table=bt64, num_pages=55)
+    b = build_decode(**kw, block_table=bt256, num_pages=15, page_size=256)
+    assert b.page_bytes == 256 * 68 and b.block_table.shape[1] == 3
+    for r, L in enumerate(kw["seq_lens"]):
+        assert np.array_equal(cache.keys(a, r, L), cache.keys(b, r, L))

@@ -145,6 +145,7 @@ class Workload:
     decode_lens: np.ndarray | None = None   # int32 [num_req], decode only
     q_packed: bool = False        # decode: q/w rows are packed tokens, not the grid
     query_lens: np.ndarray | None = None    # int32 [num_req], prefill only
+    compress_ratio: int = 1       # keys stored per request: seq_lens // compress_ratio
     meta: dict = field(default_factory=dict)
 
     @property
@@ -169,10 +170,12 @@ class Workload:
 
 
 def _fill_cache(rng, fmt, head_dim, num_pages, page_bytes, block_table, seq_lens,
-                chunk_keys=1 << 18):
+                chunk_keys=1 << 18, page_size=PAGE_SIZE):
     """Allocate the poisoned pool and write quantised N(0,1) keys into every
-    referenced slot (token t of request b -> page block_table[b, t//64],
-    slot t % 64).  Keys are drawn request by request, token order."""
+    referenced slot (key t of request b -> page block_table[b, t//page_size],
+    slot t % page_size; seq_lens here are the stored key counts).  Keys are
+    drawn request by request, token order."""
+    PAGE_SIZE = page_size  # noqa: N806 (the loop below is written for any page size)
     rb = row_bytes_for(fmt, head_dim)
     cache = np.full((num_pages, page_bytes), POISON, dtype=np.uint8)
     enc = encode_fp8_rows if fmt == "fp8" else encode_mxfp4_rows
@@ -195,10 +198,10 @@ def _fill_cache(rng, fmt, head_dim, num_pages, page_bytes, block_table, seq_lens
     return cache
 
 
-def _deal_pages(rng, seq_lens, num_pages, width):
+def _deal_pages(rng, seq_lens, num_pages, width, page_size=PAGE_SIZE):
     """Disjoint random pages for every request, dealt from one permutation of
     the pool; unused table entries are 0 (as the pages' zero-filled tables)."""
-    need = [-(-int(L) // PAGE_SIZE) for L in seq_lens]
+    need = [-(-int(L) // page_size) for L in seq_lens]
     if sum(need) > num_pages:
         raise ValueError("pool too small")
     perm = rng.permutation(num_pages).astype(np.int32)
@@ -215,36 +218,41 @@ def build_decode(*, seed: int, seq_lens, heads: int, head_dim: int, topk: int,
                  num_pages: int | None = None, pool_slack: float = 0.10,
                  width: int | None = None, w_std: float | None = None,
                  q_packed: bool = False, block_table=None, name: str = "decode",
-                 page_bytes: int | None = None) -> Workload:
+                 page_bytes: int | None = None, page_size: int = PAGE_SIZE,
+                 compress_ratio: int = 1) -> Workload:
     """A decode batch: ``num_req`` requests, the padded [num_req, next_n] grid of
-    query rows.  Draw order after the lengths: block table, keys, q, w."""
+    query rows.  With compress_ratio r, request b stores seq_lens[b] // r keys
+    (a compressed index cache).  Draw order after the lengths: block table,
+    keys, q, w."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return _build_decode_rng(rng, seq_lens=seq_lens, heads=heads, head_dim=head_dim,
                              topk=topk, fmt=fmt, next_n=next_n, decode_lens=decode_lens,
                              num_pages=num_pages, pool_slack=pool_slack, width=width,
                              w_std=w_std, q_packed=q_packed, block_table=block_table,
-                             name=name, page_bytes=page_bytes)
+                             name=name, page_bytes=page_bytes, page_size=page_size,
+                             compress_ratio=compress_ratio)
 
 
 def _build_decode_rng(rng, *, seq_lens, heads, head_dim, topk, fmt, next_n, decode_lens,
                       num_pages, pool_slack, width, w_std, q_packed, block_table, name,
-                      page_bytes):
+                      page_bytes, page_size=PAGE_SIZE, compress_ratio=1):
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = len(seq_lens)
     if decode_lens is not None:
         decode_lens = np.asarray(decode_lens, dtype=np.int32)
+    stored = seq_lens // compress_ratio
     rb = row_bytes_for(fmt, head_dim)
-    pb = page_bytes if page_bytes is not None else PAGE_SIZE * rb
-    need_pages = sum(-(-int(L) // PAGE_SIZE) for L in seq_lens)
+    pb = page_bytes if page_bytes is not None else page_size * rb
+    need_pages = sum(-(-int(L) // page_size) for L in stored)
     if num_pages is None:
         num_pages = max(1, int(math.ceil(need_pages * (1.0 + pool_slack))))
     if width is None:
-        width = max(1, -(-int(seq_lens.max(initial=1)) // PAGE_SIZE))
+        width = max(1, -(-int(stored.max(initial=1)) // page_size))
     if block_table is None:
-        block_table = _deal_pages(rng, seq_lens, num_pages, width)
+        block_table = _deal_pages(rng, stored, num_pages, width, page_size)
     else:
         block_table = np.array(block_table, dtype=np.int32, order="C", copy=True)
-    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, block_table, seq_lens)
+    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, block_table, stored, page_size=page_size)
     if q_packed:
         rows = int(decode_lens.sum()) if decode_lens is not None else B * next_n
     else:
@@ -255,34 +263,38 @@ def _build_decode_rng(rng, *, seq_lens, heads, head_dim, topk, fmt, next_n, deco
         w_std = 1.0 / math.sqrt(heads)
     w = (rng.standard_normal((rows, heads), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
     return Workload(name=name, kind="decode", fmt=fmt, heads=heads, head_dim=head_dim,
-                    topk=topk, page_size=PAGE_SIZE, page_bytes=pb, cache=cache,
+                    topk=topk, page_size=page_size, page_bytes=pb, cache=cache,
                     block_table=block_table, seq_lens=seq_lens, q=q, w=w, next_n=next_n,
-                    decode_lens=decode_lens, q_packed=q_packed)
+                    decode_lens=decode_lens, q_packed=q_packed, compress_ratio=compress_ratio)
 
 
 def build_prefill(*, seed: int, seq_lens, query_lens, heads: int, head_dim: int,
                   topk: int, fmt: str = "fp8", pool_slack: float = 0.10,
-                  w_std: float | None = None, name: str = "prefill") -> Workload:
+                  w_std: float | None = None, name: str = "prefill", page_size: int = PAGE_SIZE,
+                  compress_ratio: int = 1) -> Workload:
     """Prefill requests: request b has query_lens[b] query tokens, the last
-    ones of its seq_lens[b] keys.  q/w rows are every query token in order."""
+    ones of its seq_lens[b] tokens (seq_lens[b] // compress_ratio stored
+    keys).  q/w rows are every query token in order."""
     rng = np.random.Generator(np.random.PCG64(seed))
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     query_lens = np.asarray(query_lens, dtype=np.int32)
+    stored = seq_lens // compress_ratio
     rb = row_bytes_for(fmt, head_dim)
-    pb = PAGE_SIZE * rb
-    need_pages = sum(-(-int(L) // PAGE_SIZE) for L in seq_lens)
+    pb = page_size * rb
+    need_pages = sum(-(-int(L) // page_size) for L in stored)
     num_pages = max(1, int(math.ceil(need_pages * (1.0 + pool_slack))))
-    width = max(1, -(-int(seq_lens.max(initial=1)) // PAGE_SIZE))
-    bt = _deal_pages(rng, seq_lens, num_pages, width)
-    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, bt, seq_lens)
+    width = max(1, -(-int(stored.max(initial=1)) // page_size))
+    bt = _deal_pages(rng, stored, num_pages, width, page_size)
+    cache = _fill_cache(rng, fmt, head_dim, num_pages, pb, bt, stored, page_size=page_size)
     rows = int(query_lens.sum())
     q = _bf16_bits(rng.standard_normal((rows, heads, head_dim), dtype=np.float32))
     if w_std is None:
         w_std = 1.0 / math.sqrt(heads)
     w = (rng.standard_normal((rows, heads), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
     return Workload(name=name, kind="prefill", fmt=fmt, heads=heads, head_dim=head_dim,
-                    topk=topk, page_size=PAGE_SIZE, page_bytes=pb, cache=cache,
-                    block_table=bt, seq_lens=seq_lens, q=q, w=w, query_lens=query_lens)
+                    topk=topk, page_size=page_size, page_bytes=pb, cache=cache,
+                    block_table=bt, seq_lens=seq_lens, q=q, w=w, query_lens=query_lens,
+                    compress_ratio=compress_ratio)
 
 
 # ----------------------------------------------------------------------------
