@@ -69,12 +69,14 @@ typedef int32_t idx_status;
  * the DeepSeek-V3.2 indexer backend).  Token `slot` of page `p` is the row of
  * `row_bytes` bytes at base + p * page_bytes + slot * row_bytes, where
  * row_bytes = head_dim + 4 (fp8) or head_dim/2 + head_dim/32 (MXFP4).
+ * page_size is 64, or 256 for the compressed cache of the DeepSeek-V4
+ * indexer backend on the same page (its only supported block size).
  */
 typedef struct idx_cache {
   const void* base;    /* device, 16-byte aligned, num_pages * page_bytes bytes */
   int64_t num_pages;   /* > 0 */
   int64_t page_bytes;  /* >= page_size * row_bytes, multiple of 16 */
-  int32_t page_size;   /* tokens per page; must be 64 */
+  int32_t page_size;   /* tokens per page: 64 or 256 */
   int32_t head_dim;    /* D: fp8 32, 64 or 128; MXFP4 128 */
   int32_t fmt;         /* IDX_FMT_* */
   int32_t reserved;    /* must be 0 */
@@ -103,17 +105,19 @@ typedef struct idx_cache {
  * sum of seq_lens before b (the page's cu_seqlen_ks / cu_seqlen_ke window).
  *
  * block_table[b * bt_stride + p] is the physical page of keys
- * [64 p, 64 p + 64) of request b; only the first ceil(L/64) entries of a
- * row are read.  max_seq_len is a host upper bound of every seq_lens[b]
- * (no device read), used for sizing; seq_lens beyond it are clamped.
+ * [page_size p, page_size (p + 1)) of request b; only the first
+ * ceil(L/page_size) entries of a row are read (bt_width * page_size must
+ * cover max_seq_len / compress_ratio keys).  max_seq_len is a host upper
+ * bound of every seq_lens[b] (no device read), used for sizing; seq_lens
+ * beyond it are clamped.
  */
 typedef struct idx_rows {
   int32_t kind;                   /* IDX_ROWS_* */
   int32_t num_req;                /* >= 0 */
   const int32_t* block_table;     /* device int32 [num_req * bt_stride] */
   int64_t bt_stride;              /* elements, >= bt_width */
-  int32_t bt_width;               /* >= ceil(max_seq_len / 64) */
-  int32_t max_seq_len;            /* host bound, 0 <= max_seq_len <= bt_width * 64 */
+  int32_t bt_width;               /* >= ceil(max_seq_len / compress_ratio / page_size) */
+  int32_t max_seq_len;            /* host bound of seq_lens, >= 0 */
   const int32_t* seq_lens;        /* device int32 [num_req] */
   /* DECODE */
   const int32_t* decode_lens;     /* device int32 [num_req] or NULL */
@@ -123,6 +127,14 @@ typedef struct idx_rows {
   const int32_t* query_start_loc; /* device int32 [num_req + 1] */
   int32_t q_begin;                /* chunk query slice, 0 <= q_begin <= q_end */
   int32_t q_end;
+  /* Compressed index cache: 0 or 1 = none; r > 1 (at most 1024) = every
+   * cached key stands for r tokens.  seq_lens (and max_seq_len) stay token
+   * counts; request b holds seq_lens[b] / r keys, and every row's key count
+   * above is divided by r, rounded down (the DeepSeek-V3.2 indexer page
+   * divides its decode per-token lengths by compress_ratio and gives a
+   * prefill token (start_pos + 1 + offset) // COMPRESS_RATIO keys, its
+   * columns starting at the sum of the earlier requests' seq_lens / r). */
+  int32_t compress_ratio;
 } idx_rows;
 
 /* One prefill chunk, as planned by idx_prefill_chunks. */
@@ -168,7 +180,8 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
  *   logits device fp32; row r, column c at logits[r * logits_stride + c].
  *          DECODE writes columns [0, L); PREFILL writes [ks, ks + L).
  *          Other columns are left untouched.
- *   logits_stride >= max_seq_len (DECODE) or >= the chunk's sum of seq_lens
+ *   logits_stride >= max_seq_len / compress_ratio (DECODE) or >= the chunk's
+ *          sum of seq_lens / compress_ratio
  *          (PREFILL, the caller's N), in elements.
  */
 idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,

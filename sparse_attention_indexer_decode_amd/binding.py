@@ -51,7 +51,7 @@ class IdxRows(ctypes.Structure):
                 ("bt_stride", c_int64), ("bt_width", c_int32), ("max_seq_len", c_int32),
                 ("seq_lens", c_void_p), ("decode_lens", c_void_p), ("next_n", c_int32),
                 ("q_packed", c_int32), ("query_start_loc", c_void_p), ("q_begin", c_int32),
-                ("q_end", c_int32)]
+                ("q_end", c_int32), ("compress_ratio", c_int32)]
 
 
 class IdxChunk(ctypes.Structure):
@@ -159,22 +159,23 @@ class Rows:
 
     @staticmethod
     def decode(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, next_n: int = 1,
-               decode_lens: torch.Tensor | None = None, q_packed: bool = False) -> "Rows":
+               decode_lens: torch.Tensor | None = None, q_packed: bool = False,
+               compress_ratio: int = 1) -> "Rows":
         for t in (block_table, seq_lens, decode_lens):
             assert t is None or t.dtype == torch.int32
         c = IdxRows(IDX_ROWS_DECODE, seq_lens.shape[0], _ptr(block_table), _row_stride(block_table),
                     block_table.shape[1], int(max_seq_len), _ptr(seq_lens), _ptr(decode_lens), next_n,
-                    int(q_packed), None, 0, 0)
+                    int(q_packed), None, 0, 0, int(compress_ratio))
         return Rows(c, (block_table, seq_lens, decode_lens))
 
     @staticmethod
     def prefill(block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
-                q_begin: int, q_end: int, max_seq_len: int) -> "Rows":
+                q_begin: int, q_end: int, max_seq_len: int, compress_ratio: int = 1) -> "Rows":
         for t in (block_table, seq_lens, query_start_loc):
             assert t.dtype == torch.int32
         c = IdxRows(IDX_ROWS_PREFILL, seq_lens.shape[0], _ptr(block_table), _row_stride(block_table),
                     block_table.shape[1], int(max_seq_len), _ptr(seq_lens), None, 1, 0,
-                    _ptr(query_start_loc), int(q_begin), int(q_end))
+                    _ptr(query_start_loc), int(q_begin), int(q_end), int(compress_ratio))
         return Rows(c, (block_table, seq_lens, query_start_loc))
 
 

@@ -1,6 +1,7 @@
 // Index-cache write for gfx950: quantise new bf16 key tokens and store each
-// token's row at its int64 page slot (page = slot / 64, row = slot % 64) of
-// the paged cache; negative slots are skipped.
+// token's row at its int64 page slot (page = slot / page_size, row = slot %
+// page_size, page_size 64 or 256) of the paged cache; negative slots are
+// skipped.
 //
 // Row formats (the ones the scorer reads):
 //   fp8    D e4m3fn codes, then the fp32 per-token scale.  scale = amax / 448
@@ -28,6 +29,7 @@ struct CacheWriteParams {
   uint8_t* base;
   int64_t num_pages;
   int64_t page_bytes;
+  int32_t page_shift;  // log2(page_size / 64)
   const uint16_t* k;
   int64_t k_stride;  // elements between tokens
   const int64_t* slots;
@@ -72,10 +74,13 @@ __device__ __forceinline__ bool write_tokens(const CacheWriteParams& p, bool liv
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
 
-  const int64_t capacity = p.num_pages * kPage;
+  const int rows_log2 = 6 + p.page_shift;  // token rows per page: 64 or 256
+  const int64_t capacity = p.num_pages << rows_log2;
   const bool bad = live && slot >= capacity;
   const bool store = live && slot >= 0 && slot < capacity;
-  uint8_t* row = p.base + (store ? (slot >> 6) * p.page_bytes + (slot & 63) * kRowBytes : 0);
+  uint8_t* row = p.base + (store ? (slot >> rows_log2) * p.page_bytes +
+                                       (slot & ((int64_t{1} << rows_log2) - 1)) * kRowBytes
+                                 : 0);
 
   if constexpr (!MX) {
     amax = group_max<kLanes>(amax);

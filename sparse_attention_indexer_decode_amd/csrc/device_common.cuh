@@ -172,12 +172,20 @@ __device__ __forceinline__ void even_split(uint32_t total, uint32_t parts, uint3
 }
 
 // Key count of grid row (b, i) of a decode batch: position + 1 for real
-// tokens, 0 for padded slots; clamped to [0, max_len].
-__device__ __forceinline__ int decode_row_len(int seq, int dl, int i, int max_len) {
+// tokens, 0 for padded slots; clamped to [0, max_len], then divided by the
+// compress ratio (rounded down) for a compressed index cache.
+__device__ __forceinline__ int decode_row_len(int seq, int dl, int i, int max_len, int ratio) {
   if (i >= dl) return 0;
   int L = seq - dl + i + 1;
   L = L < 0 ? 0 : L;
-  return L > max_len ? max_len : L;
+  L = L > max_len ? max_len : L;
+  return ratio == 1 ? L : L / ratio;
+}
+
+// Stored keys of a request of `seq` tokens (clamped to [0, max_len]).
+__device__ __forceinline__ int request_keys(int seq, int max_len, int ratio) {
+  seq = seq > max_len ? max_len : (seq < 0 ? 0 : seq);
+  return ratio == 1 ? seq : seq / ratio;
 }
 
 }  // namespace idx

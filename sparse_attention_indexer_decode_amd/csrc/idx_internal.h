@@ -11,6 +11,7 @@ constexpr int kMaxGroups = 2048;   // row groups per scorer launch (LDS table)
 constexpr int kMaxK = 4096;        // top-k
 constexpr int kMaxReqPrefill = 256;  // requests per prefill chunk / packed decode batch
 constexpr int kStatusBytes = 256;  // workspace header: status word + pad
+constexpr int kMaxRatio = 1024;    // compress ratio of a compressed index cache
 
 // Workspace header layout (int32 slots).
 constexpr int kHdrStatus = 0;
@@ -21,6 +22,7 @@ struct CacheArgs {
   const uint8_t* base;
   int64_t num_pages;
   int64_t page_bytes;
+  int32_t page_shift;  // log2(page_size / 64): a page holds 1 << page_shift 64-key units
   int32_t head_dim;
   int32_t row_bytes;
   int32_t fmt;  // 0 fp8, 1 mxfp4
@@ -31,7 +33,9 @@ struct RowArgs {
   int32_t num_req;
   const int32_t* block_table;
   int64_t bt_stride;
-  int32_t max_len;
+  int32_t max_len;   // clamp of seq_lens (uncompressed tokens)
+  int32_t ratio;     // compress ratio >= 1: a row of L tokens sees L / ratio keys
+  int32_t max_keys;  // max_len / ratio
   const int32_t* seq_lens;
   const int32_t* decode_lens;
   int32_t next_n;

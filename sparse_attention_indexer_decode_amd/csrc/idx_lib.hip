@@ -45,7 +45,7 @@ int device_cu_count() {
 idx_status check_cache(const idx_cache* c, CacheArgs& out) {
   if (!c || !c->base) return fail(IDX_EINVAL, "cache descriptor or its base pointer is null");
   if (c->num_pages <= 0 || c->page_bytes <= 0 || c->reserved != 0) return fail(IDX_EINVAL, "cache: num_pages and page_bytes must be positive, reserved 0");
-  if (c->page_size != kPage) return fail(IDX_EUNSUPPORTED, "cache: page_size must be 64");
+  if (c->page_size != kPage && c->page_size != 4 * kPage) return fail(IDX_EUNSUPPORTED, "cache: page_size must be 64 or 256");
   if (c->fmt == IDX_FMT_FP8_E4M3) {
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return fail(IDX_EUNSUPPORTED, "cache: fp8 head_dim must be 32, 64 or 128");
   } else if (c->fmt == IDX_FMT_MXFP4) {
@@ -54,11 +54,14 @@ idx_status check_cache(const idx_cache* c, CacheArgs& out) {
     return fail(IDX_EUNSUPPORTED, "cache: unknown format");
   }
   const int rb = row_bytes(c->fmt, c->head_dim);
-  if (c->page_bytes < static_cast<int64_t>(kPage) * rb) return fail(IDX_EINVAL, "cache: page_bytes smaller than 64 token rows");
+  if (c->page_bytes < static_cast<int64_t>(c->page_size) * rb) return fail(IDX_EINVAL, "cache: page_bytes smaller than page_size token rows");
+  const int shift = c->page_size == kPage ? 0 : 2;
+  if (c->num_pages > (INT32_MAX >> shift)) return fail(IDX_EUNSUPPORTED, "cache: more than 2^31 64-token units");
   if ((c->page_bytes & 15) != 0 || (reinterpret_cast<uintptr_t>(c->base) & 15) != 0) return fail(IDX_EINVAL, "cache: base and page_bytes must be 16-byte aligned");
   out.base = static_cast<const uint8_t*>(c->base);
   out.num_pages = c->num_pages;
   out.page_bytes = c->page_bytes;
+  out.page_shift = shift;
   out.head_dim = c->head_dim;
   out.row_bytes = rb;
   out.fmt = c->fmt;
@@ -87,8 +90,9 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   if (need_table) {
     if (r->num_req > 0 && !r->block_table) return fail(IDX_EINVAL, "rows: block_table is null");
     if (r->bt_width < 0 || r->bt_stride < r->bt_width) return fail(IDX_EINVAL, "rows: bt_stride < bt_width");
-    if (static_cast<int64_t>(r->max_seq_len) > static_cast<int64_t>(r->bt_width) * kPage) return fail(IDX_EINVAL, "rows: max_seq_len exceeds bt_width * 64");
   }
+  if (r->compress_ratio < 0) return fail(IDX_EINVAL, "rows: compress_ratio < 0");
+  if (r->compress_ratio > kMaxRatio) return fail(IDX_EUNSUPPORTED, "rows: compress_ratio above 1024");
   if (nrows > (int64_t{1} << 30)) return fail(IDX_EUNSUPPORTED, "rows: more than 2^30 rows");
   if (r->kind == IDX_ROWS_DECODE) {
     if (r->q_packed != 0 && r->q_packed != 1) return fail(IDX_EINVAL, "rows: q_packed must be 0 or 1");
@@ -103,6 +107,8 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   out.block_table = r->block_table;
   out.bt_stride = r->bt_stride;
   out.max_len = r->max_seq_len;
+  out.ratio = r->compress_ratio > 1 ? r->compress_ratio : 1;
+  out.max_keys = out.max_len / out.ratio;
   out.seq_lens = r->seq_lens;
   out.decode_lens = r->decode_lens;
   out.next_n = r->kind == IDX_ROWS_DECODE ? r->next_n : 1;
@@ -111,6 +117,14 @@ idx_status check_rows(const idx_rows* r, bool need_table, RowArgs& out) {
   out.q_begin = r->q_begin;
   out.q_end = r->q_end;
   out.num_rows = static_cast<int32_t>(nrows);
+  return IDX_OK;
+}
+
+// The block table covers every key of the longest row: ceil(max_keys /
+// page_size) <= bt_width.
+idx_status check_table(const idx_rows* r, const RowArgs& R, const CacheArgs& C) {
+  const int64_t page = int64_t{kPage} << C.page_shift;
+  if ((R.max_keys + page - 1) / page > r->bt_width) return fail(IDX_EINVAL, "rows: max_seq_len / compress_ratio exceeds bt_width * page_size");
   return IDX_OK;
 }
 
@@ -125,7 +139,7 @@ int64_t group_bound(const RowArgs& R, int rg) {
 }
 
 int64_t scratch_stride(const RowArgs& R) {
-  const int64_t m = R.max_len > 0 ? R.max_len : 1;
+  const int64_t m = R.max_keys > 0 ? R.max_keys : 1;
   return ceil_div(m, 64) * 64;
 }
 
@@ -178,7 +192,7 @@ hipError_t dispatch_score(const ScoreParams& p, int grid, hipStream_t s) {
 // One workgroup per CU (each wave streams a contiguous page range), fewer
 // when the launch cannot hold a page per wave.
 int score_grid(const RowArgs& R, int rg) {
-  const int64_t pages = group_bound(R, rg) * ceil_div(R.max_len, kPage);
+  const int64_t pages = group_bound(R, rg) * ceil_div(R.max_keys, kPage);
   int64_t g = device_cu_count();
   const int64_t need = ceil_div(pages, 8);
   if (g > need) g = need;
@@ -205,7 +219,7 @@ idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, in
   // Batches whose rows may exceed the register path and that have at least
   // two rows per CU run a streaming-only 512-thread kernel, several rows per
   // CU at once; otherwise one 1024-thread workgroup per row.
-  if (R.max_len > kRowCap && R.num_rows >= 2 * device_cu_count())
+  if (R.max_keys > kRowCap && R.num_rows >= 2 * device_cu_count())
     hipLaunchKernelGGL((topk_kernel<kTopkThreadsLean, false>), dim3(R.num_rows), dim3(kTopkThreadsLean), 0, s, p);
   else
     hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), 0, s, p);
@@ -258,13 +272,14 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
   idx_status st = check_cache(cache, C);
   if (st != IDX_OK) return st;
   if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
+  if ((st = check_table(rows, R, C)) != IDX_OK) return st;
   if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
   if (!logits || logits_stride < 0) return fail(IDX_EINVAL, "logits is null or logits_stride < 0");
-  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
+  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_keys) return fail(IDX_EINVAL, "logits_stride < max_seq_len / compress_ratio");
   if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
   const int rg = pick_rg(R);
   if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
-  if (R.num_rows == 0 || R.max_len == 0) return IDX_OK;
+  if (R.num_rows == 0 || R.max_keys == 0) return IDX_OK;
   ScoreParams p{};
   p.cache = C;
   p.rows = R;
@@ -296,6 +311,7 @@ idx_status idx_cache_write(const idx_cache* cache, const uint16_t* k, int64_t k_
   p.base = const_cast<uint8_t*>(C.base);
   p.num_pages = C.num_pages;
   p.page_bytes = C.page_bytes;
+  p.page_shift = C.page_shift;
   p.k = k;
   p.k_stride = k_stride;
   p.slots = slot_mapping;
@@ -321,7 +337,7 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
   if (!logits || !out || logits_stride < 0) return fail(IDX_EINVAL, "logits or out is null, or logits_stride < 0");
   if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
   if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
-  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_len) return fail(IDX_EINVAL, "logits_stride < max_seq_len");
+  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_keys) return fail(IDX_EINVAL, "logits_stride < max_seq_len / compress_ratio");
   if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
   return launch_topk(logits, logits_stride, R, k, out, static_cast<hipStream_t>(stream));
@@ -336,6 +352,7 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
   if (st != IDX_OK) return st;
   if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
   if (R.kind != IDX_ROWS_DECODE) return fail(IDX_EINVAL, "idx_decode_topk takes DECODE rows");
+  if ((st = check_table(rows, R, C)) != IDX_OK) return st;
   if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
   if (!out) return fail(IDX_EINVAL, "out is null");
   if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
@@ -349,7 +366,7 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* logits = reinterpret_cast<float*>(ws + scratch_offset());
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (R.max_len > 0) {
+  if (R.max_keys > 0) {
     ScoreParams p{};
     p.cache = C;
     p.rows = R;

@@ -157,7 +157,7 @@ __device__ __forceinline__ GroupDesc describe_group(const RowArgs& R, const int 
       const int i = j * RG + r;
       const bool exists = i < R.next_n;
       real[r] = exists && i < dl;
-      L[r] = exists ? decode_row_len(seq, dl, i, R.max_len) : 0;
+      L[r] = exists ? decode_row_len(seq, dl, i, R.max_len, R.ratio) : 0;
       if (R.q_packed) qload[r] = real[r] ? req_tab[0][b] + i : -1;
       else qload[r] = exists ? b * R.next_n + i : -1;
       d.nrows += exists ? 1 : 0;
@@ -179,6 +179,7 @@ __device__ __forceinline__ GroupDesc describe_group(const RowArgs& R, const int 
       const bool exists = r < d.nrows;
       int Lr = seq - qlen + j0 + r + 1;
       Lr = Lr < 0 ? 0 : (Lr > seq ? seq : Lr);
+      Lr = R.ratio == 1 ? Lr : Lr / R.ratio;
       L[r] = exists ? Lr : 0;
       real[r] = exists;
       qload[r] = exists ? first_row + r : -1;
@@ -221,7 +222,7 @@ __device__ int build_request_tables(const RowArgs& R, SM& sm) {
       rows_b = hi > lo ? hi - lo : 0;
       first_j = lo - s;
       const int seq = R.seq_lens[b];
-      cols_b = seq > R.max_len ? R.max_len : (seq < 0 ? 0 : seq);
+      cols_b = request_keys(seq, R.max_len, R.ratio);
     }
     int tg, tr, tc;
     const int eg = block_exclusive_scan<NT>((rows_b + RG - 1) / RG, tg, sm.misc);
@@ -376,13 +377,16 @@ __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (
 // Direct global -> LDS page loads
 // ---------------------------------------------------------------------------
 
-// Requests page `phys` into the LDS buffer at byte address `lds`: byte i of
-// the page lands at lds + i.  Always issues exactly kLoads loads.
+// Requests 64-key unit `phys` (see page_ids) into the LDS buffer at byte
+// address `lds`: byte i of the unit lands at lds + i.  Always issues exactly
+// kLoads loads.
 template <int D, bool MX>
 __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_t lds) {
   using Geo = Geometry<D, MX>;
   const int lane = lane_id();
-  const uint8_t* src = p.cache.base + static_cast<int64_t>(phys) * p.cache.page_bytes;
+  const int sh = p.cache.page_shift;
+  const uint8_t* src = p.cache.base + static_cast<int64_t>(phys >> sh) * p.cache.page_bytes +
+                       (phys & ((1 << sh) - 1)) * Geo::kPageBytes;
 #pragma unroll
   for (int c = 0; c < Geo::kWide; ++c) lds_dma16(src + 1024 * c + 16 * lane, lds + 1024 * c);
 #pragma unroll
@@ -530,8 +534,10 @@ __device__ __forceinline__ int group_of_page(const int* page_prefix, int ng, int
   return lo;
 }
 
-// Block-table entries of global pages jb + lane (one per lane, 0 past j1);
-// checked against the pool where they are used.
+// Unit ids of global pages jb + lane (one per lane, 0 past j1): a cache
+// page of 64 << page_shift keys is 1 << page_shift units of 64 keys, unit
+// id = page << page_shift | unit within the page; -1 for a block-table
+// entry outside the pool (reported where it is used).
 template <int RG>
 __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_prefix,
                                         const int (*req_tab)[kMaxReqPrefill + 1], int ng, int jb, int j1) {
@@ -540,7 +546,11 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
   const RowArgs& R = p.rows;
   const int g = group_of_page(page_prefix, ng, j);
   const int b = group_request<RG>(R, req_tab, g);
-  return R.block_table[static_cast<int64_t>(b) * R.bt_stride + (j - page_prefix[g])];
+  const int u = j - page_prefix[g];  // 64-key unit of the request
+  const int sh = p.cache.page_shift;
+  const int e = R.block_table[static_cast<int64_t>(b) * R.bt_stride + (u >> sh)];
+  const bool ok = e >= 0 && static_cast<int64_t>(e) < p.cache.num_pages;
+  return ok ? (e << sh) | (u & ((1 << sh) - 1)) : -1;  // unit id, or -1 outside the pool
 }
 
 // The row of group g (decode groups hold one row): its query fragments,
@@ -626,7 +636,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
         ids = page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
       }
       const int id = __builtin_amdgcn_readlane(ids, j - jb);
-      const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
+      const bool ok = id >= 0;
       bad_page |= !ok;  // ids outside the pool read page 0 and are reported
       return ok ? id : 0;
     };
@@ -818,7 +828,7 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
       ids = page_ids<kBlockRows>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
     }
     const int id = __builtin_amdgcn_readlane(ids, j - jb);
-    const bool ok = id >= 0 && static_cast<int64_t>(id) < p.cache.num_pages;
+    const bool ok = id >= 0;
     bad_page |= !ok;  // ids outside the pool read page 0 and are reported
     return ok ? id : 0;
   };

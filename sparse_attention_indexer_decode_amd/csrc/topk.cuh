@@ -28,7 +28,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     int seq = R.seq_lens[b];
     seq = seq > R.max_len ? R.max_len : seq;
     const int dl = R.decode_lens ? R.decode_lens[b] : R.next_n;
-    L = decode_row_len(seq, dl, i, R.max_len);
+    L = decode_row_len(seq, dl, i, R.max_len, R.ratio);
   } else {
     // request of chunk token q_begin + r, then its column base
     const int q0 = R.qsl[0];
@@ -45,8 +45,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     const int b = info[0];
     int part = 0;
     for (int j = threadIdx.x; j < b; j += NT) {
-      const int s = R.seq_lens[j];
-      part += s > R.max_len ? R.max_len : (s < 0 ? 0 : s);
+      part += request_keys(R.seq_lens[j], R.max_len, R.ratio);
     }
     col0 = block_sum_int(part, sm.scan, NT);
     int seq = R.seq_lens[b];
@@ -55,6 +54,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     const int j = tok - (R.qsl[b] - q0);
     L = seq - qlen + j + 1;
     L = L < 0 ? 0 : (L > seq ? seq : L);
+    L = R.ratio == 1 ? L : L / R.ratio;
   }
   select_row<NT, kReg>(p.logits + static_cast<int64_t>(r) * p.stride + col0, L, p.k,
                  p.out + static_cast<int64_t>(r) * p.k, sm);

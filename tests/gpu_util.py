@@ -26,7 +26,8 @@ class Dev:
         self.wl = wl
         d = torch.device(device)
         self.device = d
-        self.cache = idx.Cache(torch.from_numpy(wl.cache).to(d), wl.head_dim, wl.fmt)
+        self.cache = idx.Cache(torch.from_numpy(wl.cache).to(d), wl.head_dim, wl.fmt, wl.page_size)
+        self.ratio = getattr(wl, "compress_ratio", 1)
         self.bt = torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(d)
         self.seq = torch.from_numpy(wl.seq_lens).to(d)
         self.dl = None if wl.decode_lens is None else torch.from_numpy(wl.decode_lens).to(d)
@@ -40,14 +41,14 @@ class Dev:
     def decode_rows(self):
         wl = self.wl
         return idx.Rows.decode(self.bt, self.seq, self.max_len, next_n=wl.next_n, decode_lens=self.dl,
-                               q_packed=wl.q_packed)
+                               q_packed=wl.q_packed, compress_ratio=self.ratio)
 
     def prefill_rows(self, rec):
         """Rows of a chunk record (requests [req_begin, req_end), query slice)."""
         b0, b1 = rec["req_begin"], rec["req_end"]
         qsl = self.qsl[b0 : b1 + 1]
         return idx.Rows.prefill(self.bt[b0:b1], self.seq[b0:b1], qsl, rec["q_begin"], rec["q_end"],
-                                int(self.wl.seq_lens[b0:b1].max(initial=0)))
+                                int(self.wl.seq_lens[b0:b1].max(initial=0)), compress_ratio=self.ratio)
 
     def chunk_queries(self, rec):
         t0, t1 = rec["token_begin"], rec["token_end"]

@@ -203,3 +203,18 @@ def test_cache_write_validation_and_workspace(lib):
     assert w(wsb=16) == S
     assert w(ws=FAKE + 8) == E
     assert w(n=0) == B.IDX_OK                  # nothing to enqueue
+
+
+def test_compressed_cache_validation(lib):
+    """Page size 256 and the compress ratio are checked on the host."""
+    E, U = B.IDX_EINVAL, B.IDX_EUNSUPPORTED
+    c256 = _cache(page_size=256, page_bytes=256 * 132)
+    assert _logits(lib, _cache(page_size=128), _rows()) == U
+    assert _logits(lib, _cache(page_size=256, page_bytes=64 * 132), _rows()) == E       # 256 rows do not fit
+    assert _logits(lib, c256, _rows(max_seq_len=8 * 256 + 1)) == E                      # table too narrow
+    assert _logits(lib, _cache(), _rows(max_seq_len=4 * 8 * 64 + 4, compress_ratio=4)) == E
+    assert _logits(lib, _cache(), _rows(compress_ratio=-1)) == E
+    assert _logits(lib, _cache(), _rows(compress_ratio=5000)) == U
+    # the decode logits stride has to hold max_seq_len / ratio keys
+    assert _logits(lib, _cache(), _rows(max_seq_len=400, compress_ratio=4), stride=99) == E
+    assert b"compress_ratio" in lib.idx_last_error()
