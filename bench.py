@@ -57,6 +57,8 @@ CALIB_SUBSTR = "AUnaryFunctor<float, float, float, at::native::binary_internal::
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
 DECODE_WORKLOADS = {
     "C1": "tiny fp8 decode: 1 request, L=300, 8-page pool, H=4, head_dim 32, top-k 64",
+    "V4": "compressed fp8 decode: 64 requests x 131072 tokens, compress ratio 4 (32768 keys each), 256-token "
+          "pages, H=64, head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
     "C2": "fp8 decode batch: 32 requests, next_n=1, seq_len ~ U[4096, 32768], page 64, 20k-page pool, H=64, "
           "head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
     "C3": "MTP decode: 128 requests, next_n=2 padded grid, decode_lens in {1, 2}, seq_len log-uniform in "
@@ -79,9 +81,10 @@ def algorithmic_bytes(wl) -> dict:
     (D fp8 codes + 4-byte scale = 132 B at D=128), one fp32 logit written per
     key (4 B), each row's bf16 q and fp32 w, the block-table entries of the
     live pages and the lengths."""
-    keys = int(wl.seq_lens.astype("int64").sum())
+    stored = wl.seq_lens.astype("int64") // wl.compress_ratio
+    keys = int(stored.sum())
     rows = wl.num_req * wl.next_n
-    pages = int(sum(-(-int(L) // 64) for L in wl.seq_lens))
+    pages = int(sum(-(-int(L) // wl.page_size) for L in stored))
     b = {
         "keys": keys * wl.row_bytes,
         "logits": keys * 4,
@@ -101,7 +104,7 @@ def scored_keys(wl) -> int:
     for b in range(wl.num_req):
         dl = wl.next_n if wl.decode_lens is None else int(wl.decode_lens[b])
         for i in range(min(dl, wl.next_n)):
-            L = int(wl.seq_lens[b]) - dl + i + 1
+            L = (int(wl.seq_lens[b]) - dl + i + 1) // wl.compress_ratio
             total += L if L > wl.topk else 0
     return total
 
@@ -163,18 +166,19 @@ def run(args):
     pools = [torch.from_numpy(wl.cache).to(dev)]
     for _ in range(args.copies - 1):
         pools.append(pools[0].clone())
-    caches = [idx.Cache(p, wl.head_dim, wl.fmt) for p in pools]
+    caches = [idx.Cache(p, wl.head_dim, wl.fmt, wl.page_size) for p in pools]
     bt = torch.from_numpy(wl.block_table).to(dev)
     seq = torch.from_numpy(wl.seq_lens).to(dev)
     dl = None if wl.decode_lens is None else torch.from_numpy(wl.decode_lens).to(dev)
-    rows = idx.Rows.decode(bt, seq, int(wl.seq_lens.max()), next_n=wl.next_n, decode_lens=dl)
+    rows = idx.Rows.decode(bt, seq, int(wl.seq_lens.max()), next_n=wl.next_n, decode_lens=dl,
+                           compress_ratio=wl.compress_ratio)
     q = torch.from_numpy(wl.q.view(np.int16)).to(dev).view(torch.bfloat16)
     w = torch.from_numpy(wl.w).to(dev)
     k = wl.topk
     R = rows.num_rows
     outs = torch.empty((R, k), dtype=torch.int32, device=dev)
     ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, caches[0], rows, wl.heads, k), dev)
-    ML = int(wl.seq_lens.max())
+    ML = int(wl.seq_lens.max()) // wl.compress_ratio   # keys of the longest row
     stride = -(-ML // 64) * 64
     logits = torch.empty((R, stride), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()

@@ -12,7 +12,7 @@ from workloads import cache_write_inputs
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # fmt, head_dim, tokens, num_pages, k_stride
+    # fmt, head_dim, tokens, num_pages, k_stride[, page_size]
     ("fp8", 128, 3001, 60, None),
     ("fp8", 128, 517, 9, 136),
     ("fp8", 64, 2003, 40, None),
@@ -20,13 +20,15 @@ CASES = [
     ("mxfp4", 128, 3001, 60, None),
     ("mxfp4", 128, 7, 1, 144),
     ("fp8", 128, 1, 1, None),
+    ("fp8", 128, 3001, 15, None, 256),
+    ("mxfp4", 128, 1000, 5, 136, 256),
 ]
 
 
 def _run(x, slots=None):
     dev = torch.device("cuda")
     pool = torch.from_numpy(x.cache.copy()).to(dev)
-    cache = idx.Cache(pool, x.head_dim, x.fmt)
+    cache = idx.Cache(pool, x.head_dim, x.fmt, x.page_size)
     k = torch.from_numpy(x.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     s = torch.from_numpy(x.slots if slots is None else slots).to(dev)
     ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_CACHE_WRITE, cache, None, 0, 0), dev)
@@ -37,12 +39,13 @@ def _run(x, slots=None):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_cache_write_bitexact(case):
-    fmt, D, T, P, stride = case
+    fmt, D, T, P, stride = case[:5]
+    ps = case[5] if len(case) > 5 else 64
     x = cache_write_inputs(seed=500 + CASES.index(case), tokens=T, head_dim=D, fmt=fmt, num_pages=P,
-                           k_stride=stride)
+                           k_stride=stride, page_size=ps)
     print(f"case {case} skipped slots {(x.slots < 0).sum()}", flush=True)
     got, status = _run(x)
-    ref, bad = oracle.cache_write.write(x.cache, x.k_bits[:, :D], x.slots, fmt=fmt, page_size=64,
+    ref, bad = oracle.cache_write.write(x.cache, x.k_bits[:, :D], x.slots, fmt=fmt, page_size=ps,
                                         page_bytes=x.page_bytes)
     assert not bad and status == 0
     diff = np.nonzero(got != ref)[0]

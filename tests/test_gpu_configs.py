@@ -5,7 +5,9 @@ C1, C2: every row (logits, top-k on the GPU's logits end to end, top-k on
         the oracle's fp32 logits bit-exact, idx_decode_topk end to end).
 C3, C4: the GPU runs the whole batch; the oracle checks a sample of
         requests one by one (short, long, padded, causal-fill), and the
-        invariants are checked on every row.
+        invariants are checked on every row.  The same for V4, the
+        compressed-cache decode (64 x 131072 tokens at ratio 4, 256-token
+        pages).
 C5:     the planner's 16 chunks; per chunk the GPU scores and selects all
         rows, the oracle checks sampled rows, invariants on every row.
 """
@@ -84,7 +86,7 @@ def _sample_requests(wl, n):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name,n", [("C3", 10), ("C4", 3)])
+@pytest.mark.parametrize("name,n", [("C3", 10), ("C4", 3), ("V4", 3)])
 def test_decode_config_sampled(name, n):
     wl, dev, got, out, L = _decode_full(name)
     reqs = _sample_requests(wl, n)

@@ -315,6 +315,8 @@ def config(name: str) -> Workload:
        next_n=2 padded grid, L = floor(exp(U(ln 512, ln 131072))).
     C4 MXFP4 long-context decode: 64 requests x L=131072, H=64, D=128, k=2048.
     C5 chunked prefill: 2 requests, query 16384 of seq 65536 each.
+    V4 (beyond the five) compressed fp8 decode: 64 requests x 131072 tokens at
+       compress ratio 4, 256-token pages, H=64, D=128, k=2048, seed 5.
     """
     if name == "C1":
         rng = np.random.Generator(np.random.PCG64(0))
@@ -351,6 +353,16 @@ def config(name: str) -> Workload:
         return build_prefill(seed=4, seq_lens=[65536, 65536], query_lens=[16384, 16384],
                              heads=64, head_dim=128, topk=2048, fmt="fp8", w_std=1.0 / 8,
                              name="C5")
+    if name == "V4":
+        # compressed index cache: C4's lengths at compress ratio 4 in fp8,
+        # 256-token pages (32768 keys per request)
+        rng = np.random.Generator(np.random.PCG64(5))
+        seq = np.full(64, 131072, dtype=np.int32)
+        return _build_decode_rng(rng, seq_lens=seq, heads=64, head_dim=128, topk=2048,
+                                 fmt="fp8", next_n=1, decode_lens=None, num_pages=None,
+                                 pool_slack=0.10, width=128, w_std=1.0 / 8, q_packed=False,
+                                 block_table=None, name="V4", page_bytes=None, page_size=256,
+                                 compress_ratio=4)
     raise KeyError(name)
 
 
@@ -367,11 +379,12 @@ class CacheWriteInputs:
     num_pages: int
     page_bytes: int
     cache: np.ndarray         # uint8 [num_pages, page_bytes], the cache before the write
+    page_size: int = PAGE_SIZE
 
 
 def cache_write_inputs(*, seed: int, tokens: int, head_dim: int, fmt: str, num_pages: int,
                        k_stride: int | None = None, skip_frac: float = 0.05,
-                       special_rows: bool = True) -> CacheWriteInputs:
+                       special_rows: bool = True, page_size: int = PAGE_SIZE) -> CacheWriteInputs:
     """New key tokens for an index-cache write: bf16 keys N(0,1) times a
     per-token power of two in [2^-20, 2^20], distinct random slots of the
     pool (a fraction set to -1, i.e. not stored) and a poisoned pool.  With
@@ -413,10 +426,10 @@ def cache_write_inputs(*, seed: int, tokens: int, head_dim: int, fmt: str, num_p
     bits = np.zeros((tokens, stride), dtype=np.uint16)
     bits[:, :D] = _bf16_bits(k)
     rb = row_bytes_for(fmt, D)
-    page_bytes = (PAGE_SIZE * rb + 15) // 16 * 16
-    cap = num_pages * PAGE_SIZE
+    page_bytes = (page_size * rb + 15) // 16 * 16
+    cap = num_pages * page_size
     assert tokens <= cap
     slots = rng.permutation(cap)[:tokens].astype(np.int64)
     slots[rng.random(tokens) < skip_frac] = -1
     cache = np.full((num_pages, page_bytes), 0x5A, dtype=np.uint8)
-    return CacheWriteInputs(fmt, D, bits, slots, num_pages, page_bytes, cache)
+    return CacheWriteInputs(fmt, D, bits, slots, num_pages, page_bytes, cache, page_size)
