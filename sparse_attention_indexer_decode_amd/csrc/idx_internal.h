@@ -9,6 +9,7 @@ namespace idx {
 constexpr int kMaxHeads = 64;
 constexpr int kMaxGroups = 2048;   // row groups per scorer launch (LDS table)
 constexpr int kMaxK = 4096;        // top-k
+constexpr int kMaxTopkChunks = 4;  // chunks of a long row split over workgroups
 constexpr int kMaxReqPrefill = 256;  // requests per prefill chunk / packed decode batch
 constexpr int kStatusBytes = 256;  // workspace header: status word + pad
 constexpr int kMaxRatio = 1024;    // compress ratio of a compressed index cache

@@ -209,13 +209,46 @@ idx_status check_queries(const uint16_t* q, const float* w, int heads) {
   return IDX_OK;
 }
 
-idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, int k, int32_t* out, hipStream_t s) {
+// Rows longer than the register path (kRowCap keys) in a batch of fewer
+// than kChunkRowsMax rows are split into chunks of kRowCap keys, each chunk
+// selected by its own workgroup, then merged per row (a pure function of
+// the rows and k, so that the workspace size does not depend on the device).
+constexpr int kChunkRowsMax = 512;
+
+int topk_chunks(const RowArgs& R) {
+  if (R.max_keys <= kRowCap || R.num_rows >= kChunkRowsMax) return 0;
+  const int64_t c = ceil_div(R.max_keys, kRowCap);
+  return c <= kMaxTopkChunks ? static_cast<int>(c) : 0;
+}
+
+// Workspace bytes of the chunk candidates (three [rows][chunks][k] arrays).
+size_t topk_chunk_bytes(const RowArgs& R, int k) {
+  const int c = topk_chunks(R);
+  return c ? align_up(3 * sizeof(int32_t) * static_cast<size_t>(R.num_rows) * c * k, 256) : 0;
+}
+
+idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, int k, int32_t* out,
+                       void* chunk_ws, hipStream_t s) {
   TopkParams p{};
   p.logits = logits;
   p.stride = stride;
   p.rows = R;
   p.k = k;
   p.out = out;
+  const int nc = topk_chunks(R);
+  if (nc > 0) {
+    const size_t n = static_cast<size_t>(R.num_rows) * nc * k;
+    p.chunks = nc;
+    p.cand = static_cast<int32_t*>(chunk_ws);
+    p.cand_val = reinterpret_cast<float*>(p.cand + n);
+    p.cand_pos = reinterpret_cast<int32_t*>(p.cand_val + n);
+    // unused dynamic LDS that keeps two of these workgroups off one CU (the
+    // launch has at most a few hundred; doubling up would halve their speed)
+    constexpr unsigned kOneWgPerCu = 48 * 1024;
+    hipLaunchKernelGGL(topk_chunk_kernel<kTopkThreads>, dim3(R.num_rows * nc), dim3(kTopkThreads), kOneWgPerCu, s, p);
+    hipLaunchKernelGGL(topk_merge_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), kOneWgPerCu, s, p);
+    return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+  }
   // Batches whose rows may exceed the register path and that have at least
   // two rows per CU run a streaming-only 512-thread kernel, several rows per
   // CU at once; otherwise one 1024-thread workgroup per row.
@@ -251,7 +284,8 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
   }
   if (op == IDX_OP_TOPK) {
     if (check_rows(rows, false, R) != IDX_OK) return 0;
-    return kStatusBytes;
+    if (k < 1 || k > kMaxK) return kStatusBytes;
+    return kStatusBytes + topk_chunk_bytes(R, k);
   }
   CacheArgs C;
   if (check_cache(cache, C) != IDX_OK || check_rows(rows, true, R) != IDX_OK) return 0;
@@ -259,7 +293,7 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
   if (op == IDX_OP_LOGITS) return kStatusBytes;
   if (op == IDX_OP_DECODE_TOPK) {
     if (R.kind != IDX_ROWS_DECODE || k < 1 || k > kMaxK) return 0;
-    return decode_ws_bytes(R);
+    return decode_ws_bytes(R) + topk_chunk_bytes(R, k);
   }
   return 0;
 }
@@ -338,9 +372,10 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
   if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
   if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
   if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_keys) return fail(IDX_EINVAL, "logits_stride < max_seq_len / compress_ratio");
-  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes + topk_chunk_bytes(R, k))) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
-  return launch_topk(logits, logits_stride, R, k, out, static_cast<hipStream_t>(stream));
+  return launch_topk(logits, logits_stride, R, k, out, static_cast<uint8_t*>(workspace) + kStatusBytes,
+                     static_cast<hipStream_t>(stream));
 }
 
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
@@ -359,7 +394,7 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
   if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
   const int rg = pick_rg(R);
   if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
-  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R))) != IDX_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R) + topk_chunk_bytes(R, k))) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
   // scorer into the workspace's row logits, then top-k of each row (the
   // kernel boundary orders the two)
@@ -379,7 +414,7 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
     p.num_groups = static_cast<int32_t>(group_bound(R, rg));
     if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
   }
-  return launch_topk(logits, scratch_stride(R), R, k, out, s);
+  return launch_topk(logits, scratch_stride(R), R, k, out, ws + decode_ws_bytes(R), s);
 }
 
 idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream) {

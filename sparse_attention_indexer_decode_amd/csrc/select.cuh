@@ -283,7 +283,7 @@ __device__ void compact_global(const float* __restrict__ row, int L, int k, bool
 
 // Top-k of a row streamed from global memory (k < L).
 template <int NT>
-__device__ void select_row_stream(const float* __restrict__ row, int L, int k, int* __restrict__ out,
+__device__ __forceinline__ void select_row_stream(const float* __restrict__ row, int L, int k, int* __restrict__ out,
                                   SelectShared<NT>& sm) {
   const int tid = threadIdx.x;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
@@ -412,7 +412,7 @@ __device__ void select_row_stream(const float* __restrict__ row, int L, int k, i
 // exponent bins the key's top bits would give; the exact 32-bit key only
 // decides within the threshold bin.
 template <int NT, int E>
-__device__ void select_row_reg(const float* __restrict__ row, int L, int k, int* __restrict__ out,
+__device__ __forceinline__ void select_row_reg(const float* __restrict__ row, int L, int k, int* __restrict__ out,
                                SelectShared<NT>& sm) {
   static_assert(E % 4 == 0, "keys per thread come in quads");
   constexpr int EQ = E / 4;  // quads per thread: quad q = tid + NT j holds keys 4q .. 4q + 3
@@ -601,7 +601,7 @@ __device__ void select_row_reg(const float* __restrict__ row, int L, int k, int*
 // longer than k streams from memory), for a lean kernel that fits several
 // workgroups per CU.
 template <int NT, bool kReg = true>
-__device__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out, SelectShared<NT>& sm) {
+__device__ __forceinline__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out, SelectShared<NT>& sm) {
   if (L <= k) {
     for (int j = threadIdx.x; j < k; j += NT) out[j] = (j < L) ? j : -1;
   } else if (kReg && L <= kRowCap) {

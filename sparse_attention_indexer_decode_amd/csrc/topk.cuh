@@ -12,14 +12,18 @@ struct TopkParams {
   RowArgs rows;
   int32_t k;
   int32_t* out;
+  // long rows split over workgroups (topk_chunk_kernel / topk_merge_kernel)
+  int32_t chunks;     // chunk slots per row (ceil(max_keys / kRowCap))
+  int32_t* cand;      // [rows][chunks][k] chunk top-k positions
+  float* cand_val;    // [rows][chunks * k] candidate logits in position order
+  int32_t* cand_pos;  // [rows][chunks * k] their positions in the row
 };
 
-// kReg: see select_row.
-template <int NT, bool kReg = true>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
-  __shared__ SelectShared<NT> sm;
-  __shared__ int info[2];
-  const int r = blockIdx.x;
+// Key count L and logits column base of row r (DECODE grid row or PREFILL
+// chunk row); every thread of the workgroup gets the same values.
+template <int NT>
+__device__ __forceinline__ void row_window(const TopkParams& p, int r, int& L_out, int& col0_out, SelectShared<NT>& sm,
+                           int (&info)[2]) {
   const RowArgs& R = p.rows;
   int L = 0, col0 = 0;
   if (R.kind == 0) {
@@ -56,8 +60,102 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     L = L < 0 ? 0 : (L > seq ? seq : L);
     L = R.ratio == 1 ? L : L / R.ratio;
   }
+  L_out = L;
+  col0_out = col0;
+}
+
+// kReg: see select_row.
+template <int NT, bool kReg = true>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
+  __shared__ SelectShared<NT> sm;
+  __shared__ int info[2];
+  const int r = blockIdx.x;
+  int L, col0;
+  row_window<NT>(p, r, L, col0, sm, info);
   select_row<NT, kReg>(p.logits + static_cast<int64_t>(r) * p.stride + col0, L, p.k,
-                 p.out + static_cast<int64_t>(r) * p.k, sm);
+                       p.out + static_cast<int64_t>(r) * p.k, sm);
+}
+
+// Rows longer than kRowCap keys split over workgroups (few rows, many CUs).
+// Chunk c of a row holds its keys [c kRowCap, min(L, (c + 1) kRowCap)); the
+// chunk's own top-k holds every key of the row's top-k that lies in it (ties
+// go to the lower position inside a chunk as in the row).  Workgroup
+// (r, c) of topk_chunk_kernel selects chunk c into cand[r][c][0 .. k); a row
+// of at most kRowCap keys is finished there by its chunk 0.  Then one
+// workgroup per long row (topk_merge_kernel) lays the candidates out in
+// position order -- chunk by chunk, each chunk's list ascending -- with their
+// logits, selects k of them with the same rule (ties to the lower candidate
+// index, which is the lower position) and writes their positions.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
+  __shared__ SelectShared<NT> sm;
+  __shared__ int info[2];
+  const int r = blockIdx.x / p.chunks;
+  const int c = blockIdx.x - r * p.chunks;
+  int L, col0;
+  row_window<NT>(p, r, L, col0, sm, info);
+  const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
+  if (L <= kRowCap) {
+    if (c == 0) select_row<NT>(row, L, p.k, p.out + static_cast<int64_t>(r) * p.k, sm);
+    return;
+  }
+  const int lo = c * kRowCap;
+  if (lo >= L) return;
+  const int Lc = L - lo < kRowCap ? L - lo : kRowCap;
+  select_row<NT>(row + lo, Lc, p.k, p.cand + (static_cast<int64_t>(r) * p.chunks + c) * p.k, sm);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
+  __shared__ SelectShared<NT> sm;
+  __shared__ int info[2];
+  const int r = blockIdx.x;
+  int L, col0;
+  row_window<NT>(p, r, L, col0, sm, info);
+  if (L <= kRowCap) return;  // finished by its chunk
+  const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
+  const int k = p.k;
+  const int nc = (L + kRowCap - 1) / kRowCap;
+  const int last = L - (nc - 1) * kRowCap;  // keys of the last chunk
+  // every chunk but the last has more than k keys (kRowCap > k): its k
+  // entries are all positions; the last has min(last, k)
+  const int n = (nc - 1) * k + (last < k ? last : k);
+  const int64_t base = static_cast<int64_t>(r) * p.chunks * k;
+  const int32_t* cand = p.cand + base;
+  float* val = p.cand_val + base;
+  int32_t* pos = p.cand_pos + base;
+  // every thread's loads are issued before any is used (two dependent
+  // round trips in all, not two per candidate)
+  constexpr int kPer = kMaxTopkChunks * kMaxK / NT;  // candidates per thread at most
+  int t[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + u * NT;
+    t[u] = i < n ? (i / k) * kRowCap + cand[i] : 0;
+  }
+  float v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) v[u] = row[t[u]];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + u * NT;
+    if (i < n) {
+      pos[i] = t[u];
+      val[i] = v[u];
+    }
+  }
+  __syncthreads();  // workgroup-scope release/acquire: the values are visible to every thread
+  int32_t* out = p.out + static_cast<int64_t>(r) * k;
+  // n > k: k candidate indices, ascending; the register path sized to n
+  // (its passes cost the keys per thread it is built for, not n)
+  if (n <= 8 * NT) select_row_reg<NT, 8>(val, n, k, out, sm);
+  else if (n <= 16 * NT) select_row_reg<NT, 16>(val, n, k, out, sm);
+  else select_row_reg<NT, kRowCap / NT>(val, n, k, out, sm);
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += NT) {
+    const int ci = out[j];
+    out[j] = pos[ci];
+  }
 }
 
 }  // namespace idx

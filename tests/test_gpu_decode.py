@@ -250,3 +250,44 @@ def test_decode_topk_in_a_hip_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, refs[i % 2]), f"replay {i}"
+
+
+@pytest.mark.parametrize("k", [64, 2048, 4096])
+def test_topk_long_rows_split_over_workgroups(k):
+    """Rows past the register path in a small batch are selected chunk by
+    chunk (32768 keys per workgroup) and merged: bit-exact against the
+    oracle, with ties that straddle chunk boundaries."""
+    rng = np.random.default_rng(41)
+    lens = [32769, 65536, 98321, 131072, 40000, 131071, 70000, 5000]
+    rows = []
+    for i, L in enumerate(lens):
+        kind = i % 4
+        if kind == 0:
+            v = np.full(L, -2.5, dtype=np.float32)                       # every key ties
+        elif kind == 1:
+            v = (rng.integers(0, 3, size=L) * 0.5).astype(np.float32)    # three levels
+            v[32760:32780] = 1.0                                          # ties across the first boundary
+        elif kind == 2:
+            v = np.linspace(1.0, -1.0, L).astype(np.float32)             # largest keys first
+            v[::2] = -0.0
+        else:
+            v = (rng.standard_normal(L) * 4).astype(np.float32)
+            v[-k:] = 100.0                                                # the top-k sits in the last chunk
+        rows.append(v)
+    R = len(lens)
+    stride = max(lens) + 5
+    buf = np.full((R, stride), np.nan, dtype=np.float32)
+    for r, v in enumerate(rows):
+        buf[r, : len(v)] = v
+    d = torch.device("cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device=d)
+    bt = torch.zeros((R, 1), dtype=torch.int32, device=d)
+    rows_d = idx.Rows.decode(bt, seq, max(lens))
+    out = torch.full((R, k), -7, dtype=torch.int32, device=d)
+    ws = topk_workspace(rows_d, k)
+    assert ws.numel() > 256                 # the chunk candidates live in the workspace
+    idx.idx_topk(torch.from_numpy(buf).to(d), rows_d, k, out, ws)
+    o = out.cpu().numpy()
+    for r, v in enumerate(rows):
+        exp = oracle.topk.topk_row(v.astype(np.float64), len(v), k)
+        assert np.array_equal(o[r], exp), f"row {r} (L={len(v)}, k={k})"
