@@ -198,6 +198,10 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
  *   logits device fp32, same layout as idx_logits_paged's output
  *   k      1..4096
  *   out    device int32 [rows, k]
+ * Workspace: idx_workspace_bytes(IDX_OP_TOPK, NULL, rows, 0, k) -- the
+ * status word, plus the chunk candidates (3 x rows x ceil(max keys / 32768)
+ * x k int32) when rows longer than 32768 keys are split over workgroups
+ * (fewer than 512 rows and at most 131072 keys per row).
  */
 idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, int32_t k,
                     int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -209,8 +213,8 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
  * into the workspace and the selector reading them.  Keys of a request are
  * read once for all its rows; rows with L <= k are causal filled; padded
  * rows get -1.  Output as idx_topk.  The workspace
- * (idx_workspace_bytes(IDX_OP_DECODE_TOPK, ...)) holds the status word and
- * the per-row logits.
+ * (idx_workspace_bytes(IDX_OP_DECODE_TOPK, ...)) holds the status word,
+ * the per-row logits and, for long rows, idx_topk's chunk candidates.
  */
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
                            const float* w, int32_t heads, int32_t k, int32_t* out,
