@@ -81,11 +81,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 // chunk's own top-k holds every key of the row's top-k that lies in it (ties
 // go to the lower position inside a chunk as in the row).  Workgroup
 // (r, c) of topk_chunk_kernel selects chunk c into cand[r][c][0 .. k); a row
-// of at most kRowCap keys is finished there by its chunk 0.  Then one
-// workgroup per long row (topk_merge_kernel) lays the candidates out in
-// position order -- chunk by chunk, each chunk's list ascending -- with their
-// logits, selects k of them with the same rule (ties to the lower candidate
-// index, which is the lower position) and writes their positions.
+// of at most kRowCap keys is finished there by its chunk 0.  The chunk also
+// writes its candidates' logits and row positions, so that a row's
+// candidates lie in position order -- chunk by chunk, each chunk's list
+// ascending.  Then one workgroup per long row (topk_merge_kernel) selects k
+// of them with the same rule (ties to the lower candidate index, which is
+// the lower position) and writes their positions.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   __shared__ SelectShared<NT> sm;
@@ -102,7 +103,18 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   const int lo = c * kRowCap;
   if (lo >= L) return;
   const int Lc = L - lo < kRowCap ? L - lo : kRowCap;
-  select_row<NT>(row + lo, Lc, p.k, p.cand + (static_cast<int64_t>(r) * p.chunks + c) * p.k, sm);
+  const int64_t slot = (static_cast<int64_t>(r) * p.chunks + c) * p.k;
+  select_row<NT>(row + lo, Lc, p.k, p.cand + slot, sm);
+  // the candidates' logits and row positions, laid out for the merge while
+  // the chunk is still in cache (every chunk but the last has more than k
+  // keys, so the row's candidates are contiguous)
+  __syncthreads();  // the selected positions are visible to every thread
+  const int m = Lc < p.k ? Lc : p.k;
+  for (int j = threadIdx.x; j < m; j += NT) {
+    const int t = lo + p.cand[slot + j];
+    p.cand_pos[slot + j] = t;
+    p.cand_val[slot + j] = row[t];
+  }
 }
 
 template <int NT>
@@ -113,7 +125,6 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   int L, col0;
   row_window<NT>(p, r, L, col0, sm, info);
   if (L <= kRowCap) return;  // finished by its chunk
-  const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
   const int k = p.k;
   const int nc = (L + kRowCap - 1) / kRowCap;
   const int last = L - (nc - 1) * kRowCap;  // keys of the last chunk
@@ -121,30 +132,8 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   // entries are all positions; the last has min(last, k)
   const int n = (nc - 1) * k + (last < k ? last : k);
   const int64_t base = static_cast<int64_t>(r) * p.chunks * k;
-  const int32_t* cand = p.cand + base;
-  float* val = p.cand_val + base;
-  int32_t* pos = p.cand_pos + base;
-  // every thread's loads are issued before any is used (two dependent
-  // round trips in all, not two per candidate)
-  constexpr int kPer = kMaxTopkChunks * kMaxK / NT;  // candidates per thread at most
-  int t[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = threadIdx.x + u * NT;
-    t[u] = i < n ? (i / k) * kRowCap + cand[i] : 0;
-  }
-  float v[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = row[t[u]];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = threadIdx.x + u * NT;
-    if (i < n) {
-      pos[i] = t[u];
-      val[i] = v[u];
-    }
-  }
-  __syncthreads();  // workgroup-scope release/acquire: the values are visible to every thread
+  const float* val = p.cand_val + base;
+  const int32_t* pos = p.cand_pos + base;
   int32_t* out = p.out + static_cast<int64_t>(r) * k;
   // n > k: k candidate indices, ascending; the register path sized to n
   // (its passes cost the keys per thread it is built for, not n)

@@ -213,11 +213,17 @@ def test_bad_page_id_flags_and_never_faults():
     assert idx.idx_read_device_status(ws) == 0      # read clears it
 
 
-def test_decode_topk_in_a_hip_graph_replays():
+@pytest.mark.parametrize("rows_kind", ["short", "long"])
+def test_decode_topk_in_a_hip_graph_replays(rows_kind):
     """idx_decode_topk captured in a HIP graph: every replay, with other
     eager work and synchronisation in between and new query contents each
-    time, gives the eager result for those contents."""
-    wl = _case("fp8", 128, 64, 2, False, seed=12)
+    time, gives the eager result for those contents.  "long" rows exceed
+    32768 keys, so the selector's chunk and merge launches are captured."""
+    if rows_kind == "short":
+        wl = _case("fp8", 128, 64, 2, False, seed=12)
+    else:
+        wl = build_decode(seed=13, seq_lens=[40000, 131072, 500, 70001], heads=16, head_dim=64, topk=256,
+                          name="graph-long")
     dev = Dev(wl)
     rows = dev.decode_rows()
     k = wl.topk
