@@ -96,3 +96,40 @@ def test_cache_write_full_size_sampled(fmt):
     # every slot was written: no row keeps the poison pattern in its scale bytes
     rows = pool[:, : 64 * rb].reshape(P * 64, rb)
     assert not bool(((rows[:, -4:] == 0x5A).all(dim=1)).any())
+
+
+@pytest.mark.parametrize("fmt,ps,ratio", [("fp8", 64, 1), ("mxfp4", 64, 1), ("fp8", 256, 4)])
+def test_written_cache_is_scored_like_the_oracles(fmt, ps, ratio):
+    """Keys written by idx_cache_write at the slots a block table gives them,
+    then scored by idx_logits_paged / idx_decode_topk, against the oracle's
+    write followed by the oracle's scoring."""
+    from tests.gpu_util import Dev, check_logits, check_topk_e2e
+    from workloads import build_decode
+
+    seqs = [70, 1000, 4100, 9000]
+    H, D, k = 32, 128, 256
+    wl = build_decode(seed=61, seq_lens=seqs, heads=H, head_dim=D, topk=k, fmt=fmt, page_size=ps,
+                      compress_ratio=ratio, name=f"written-{fmt}-p{ps}")
+    stored = np.asarray(seqs) // ratio
+    rng = np.random.default_rng(62)
+    T = int(stored.sum())
+    keys = (rng.standard_normal((T, D)).astype(np.float32) * np.exp2(rng.integers(-3, 4, (T, 1))))
+    kb = torch.from_numpy(keys).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # slot of stored key t of request b: page block_table[b, t // ps], row t % ps
+    slots = np.concatenate([wl.block_table[b, np.arange(n) // ps].astype(np.int64) * ps + np.arange(n) % ps
+                            for b, n in enumerate(stored)])
+    ref_pool, bad = oracle.cache_write.write(wl.cache, kb, slots, fmt=fmt, page_size=ps, page_bytes=wl.page_bytes)
+    assert not bad
+    dev = Dev(wl)
+    ws = idx.new_workspace(256, dev.device)
+    idx.idx_cache_write(dev.cache, torch.from_numpy(kb.view(np.int16)).to(dev.device).view(torch.bfloat16),
+                        torch.from_numpy(slots).to(dev.device), ws)
+    got_pool = dev.cache.pages.cpu().numpy().reshape(-1)
+    assert np.array_equal(got_pool, ref_pool)
+    wl.cache = ref_pool.reshape(wl.cache.shape)        # the oracle scores its own write
+    ref = oracle.pipeline.decode_logits(wl)
+    got, _ = dev.logits_decode()
+    check_logits(got, {r: v for r, v in ref.items() if len(v)}, label=wl.name)
+    L, _ = oracle.pipeline.decode_row_info(wl)
+    out, _ = dev.decode_topk()
+    check_topk_e2e(out, ref, L, k, label=wl.name)
