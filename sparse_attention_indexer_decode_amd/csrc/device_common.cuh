@@ -37,6 +37,17 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
 __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
+// The same with a wave-uniform base in scalar registers and a per-lane byte
+// offset (global address sbase + voff; no immediate offset), so that a
+// page's address arithmetic runs on the scalar unit.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS byte address of a shared-memory pointer.

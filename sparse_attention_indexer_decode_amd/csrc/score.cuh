@@ -388,10 +388,10 @@ __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_
   const uint8_t* src = p.cache.base + static_cast<int64_t>(phys >> sh) * p.cache.page_bytes +
                        (phys & ((1 << sh) - 1)) * Geo::kPageBytes;
 #pragma unroll
-  for (int c = 0; c < Geo::kWide; ++c) lds_dma16(src + 1024 * c + 16 * lane, lds + 1024 * c);
+  for (int c = 0; c < Geo::kWide; ++c) lds_dma16_s(src + 1024 * c, 16 * lane, lds + 1024 * c);
 #pragma unroll
   for (int c = 0; c < Geo::kNarrow; ++c)
-    lds_dma4(src + 1024 * Geo::kWide + 256 * c + 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
+    lds_dma4_s(src + 1024 * Geo::kWide + 256 * c, 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
 }
 
 // Waits until a page has landed in LDS, given how many pages were requested
