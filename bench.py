@@ -333,7 +333,9 @@ def run_prefill(args):
     big = max(M * N for _, _, _, M, N in chunks)
     logits_buf = torch.empty(big, dtype=torch.float32, device=dev)
     outs = torch.empty((max(c[3] for c in chunks), k), dtype=torch.int32, device=dev)
-    ws = idx.new_workspace(4096, dev)
+    ws_bytes = max(max(idx.idx_workspace_bytes(idx.IDX_OP_LOGITS, cache, c[0], wl.heads, 0),
+                       idx.idx_workspace_bytes(idx.IDX_OP_TOPK, None, c[0], 0, k)) for c in chunks)
+    ws = idx.new_workspace(ws_bytes, dev)
     stream = torch.cuda.current_stream()
 
     def one_pass(ev=None):
