@@ -77,36 +77,36 @@ struct Geometry {
   static_assert(kLoads <= 15, "loads per page must fit a vmcnt immediate");
 };
 
-// Bytes of a group's query block staged in LDS (full 32-head tiles of
-// 128 dims only; see load_query_staged).
-template <int D, int RG, int MT>
-constexpr int query_stage_bytes() { return D == 128 ? RG * MT * 32 * D * 2 : 0; }
+// Bytes of a row's query block staged in LDS (full 32-head tiles of 128
+// dims only; see load_query_staged).
+template <int D, int MT>
+constexpr int query_stage_bytes() { return D == 128 ? MT * 32 * D * 2 : 0; }
 
 // Pages in each wave's ring: as many as its LDS area holds (at least two,
 // at most four), the area being sized for two pages or for the first group's
 // staged queries, whichever is larger.
-template <int D, bool MX, int RG, int MT>
+template <int D, bool MX, int MT>
 constexpr int ring_pages() {
   constexpr int pb = Geometry<D, MX>::kPageBytes;
-  constexpr int area = 2 * pb > query_stage_bytes<D, RG, MT>() ? 2 * pb : query_stage_bytes<D, RG, MT>();
+  constexpr int area = 2 * pb > query_stage_bytes<D, MT>() ? 2 * pb : query_stage_bytes<D, MT>();
   return area / pb > 4 ? 4 : area / pb;
 }
 
 // Each wave's LDS area: its page ring, which also stages the first group's
 // queries before the first page is requested.
-template <int D, bool MX, int RG, int MT>
+template <int D, bool MX, int MT>
 union WaveArea {
-  uint8_t page[ring_pages<D, MX, RG, MT>()][Geometry<D, MX>::kPageBytes];
-  uint8_t stage[query_stage_bytes<D, RG, MT>() > 0 ? query_stage_bytes<D, RG, MT>() : 16];
+  uint8_t page[ring_pages<D, MX, MT>()][Geometry<D, MX>::kPageBytes];
+  uint8_t stage[query_stage_bytes<D, MT>() > 0 ? query_stage_bytes<D, MT>() : 16];
 };
 
-template <int D, bool MX, int RG, int MT, int NWV>
+template <int D, bool MX, int MT, int NWV>
 struct ScoreShared {
   int page_prefix[kMaxGroups + 1];     // pages before each group
   int req_tab[4][kMaxReqPrefill + 1];  // prefill: groups, rows, columns, first query; decode: packed offsets
-  float wbuf[NWV][RG][kMaxHeads];
+  float wbuf[NWV][kMaxHeads];          // each wave's head weights on their way to registers
   int misc[16];
-  alignas(16) WaveArea<D, MX, RG, MT> area[NWV];
+  alignas(16) WaveArea<D, MX, MT> area[NWV];
 };
 
 struct GroupDesc {
@@ -251,31 +251,28 @@ __device__ int build_request_tables(const RowArgs& R, SM& sm) {
 // Operand fragments
 // ---------------------------------------------------------------------------
 
-template <int D, int RG, int MT>
+template <int D, int MT>
 struct QFrag {
-  v8bf a[RG][MT][D / 16];
+  v8bf a[MT][D / 16];
 };
 
-// A fragments of the group's rows (this lane: head 32 mt + lane % 32, dims
-// [g D/2, g D/2 + D/2)).  Rows or heads that do not exist read row 0 / head 0
-// instead (loads stay unconditional); their head weights are zero, so they
-// add nothing.
-template <int D, int RG, int MT>
-__device__ __forceinline__ void load_query(const ScoreParams& p, const int (&qload)[RG], QFrag<D, RG, MT>& f) {
+// A fragments of query row `qrow` (this lane: head 32 mt + lane % 32, dims
+// [g D/2, g D/2 + D/2)).  A row (-1) or heads that do not exist read row 0 /
+// head 0 instead (loads stay unconditional); their head weights are zero, so
+// they add nothing.
+template <int D, int MT>
+__device__ __forceinline__ void load_query(const ScoreParams& p, int qrow, QFrag<D, MT>& f) {
   const int lane = lane_id();
   const int m = lane & 31;
   const int g = lane >> 5;
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 32 * mt + m;
+    const bool valid = qrow >= 0 && h < p.heads;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        p.q + (static_cast<int64_t>(valid ? qrow : 0) * p.heads + (valid ? h : 0)) * D + g * (D / 2));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int h = 32 * mt + m;
-      const bool valid = qload[r] >= 0 && h < p.heads;
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          p.q + (static_cast<int64_t>(valid ? qload[r] : 0) * p.heads + (valid ? h : 0)) * D + g * (D / 2));
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) f.a[r][mt][s] = __builtin_bit_cast(v8bf, src[s]);
-    }
+    for (int s = 0; s < D / 16; ++s) f.a[mt][s] = __builtin_bit_cast(v8bf, src[s]);
   }
 }
 
@@ -284,32 +281,27 @@ __device__ __forceinline__ void load_query(const ScoreParams& p, const int (&qlo
 // touches 64 different 128-byte lines (32 heads x 2 lane halves).  Here
 // direct global->LDS loads copy the group's query block into the area, each
 // instruction 1 KiB of contiguous query (4 heads), and the fragments are
-// read back from LDS.  Chunk c of head h (dims 8c .. 8c + 7, within row r's
-// block) sits at 16-byte slot 16 h + (c ^ (h % 16) ^ ((h / 16) % 2)): the
+// read back from LDS.  Chunk c of head h (dims 8c .. 8c + 7) sits at 16-byte
+// slot 16 h + (c ^ (h % 16) ^ ((h / 16) % 2)): the
 // XOR keeps the 16 (or 32) lanes of each b128 fragment read on distinct
 // bank groups.  The load writes lane l's 16 bytes to slot 64 i + l, so lane
 // l fetches the chunk that belongs there, a permutation within the same
 // 1 KiB.  Waits for every outstanding load before reading; the caller must
 // not reuse the area before the reads have returned.
-template <int D, int RG, int MT>
-__device__ __forceinline__ void load_query_staged(const ScoreParams& p, const int (&qload)[RG], uint8_t* area,
-                                                  QFrag<D, RG, MT>& f) {
+template <int D, int MT>
+__device__ __forceinline__ void load_query_staged(const ScoreParams& p, int qrow, uint8_t* area, QFrag<D, MT>& f) {
   static_assert(D == 128, "staging assumes 16 chunks of 16 bytes per head");
   constexpr int kHeads = 32 * MT;
   constexpr int kLoads = kHeads * D * 2 / 1024;  // 1 KiB per load instruction
   const int lane = lane_id();
   auto swz = [](int h) { return (h & 15) ^ ((h >> 4) & 1); };
   const uint32_t base = lds_addr(area);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(p.q) + static_cast<int64_t>(qrow >= 0 ? qrow : 0) * kHeads * D * 2;
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.q) +
-                         static_cast<int64_t>(qload[r] >= 0 ? qload[r] : 0) * kHeads * D * 2;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int h = 4 * i + lane / 16;
-      const int c = (lane % 16) ^ swz(h);
-      lds_dma16(src + (16 * h + c) * 16, base + r * kHeads * 256 + 1024 * i);
-    }
+  for (int i = 0; i < kLoads; ++i) {
+    const int h = 4 * i + lane / 16;
+    const int c = (lane % 16) ^ swz(h);
+    lds_dma16(src + (16 * h + c) * 16, base + 1024 * i);
   }
   wait_all_loads();
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -317,14 +309,12 @@ __device__ __forceinline__ void load_query_staged(const ScoreParams& p, const in
   const int m = lane & 31;
   const int g = lane >> 5;
 #pragma unroll
-  for (int r = 0; r < RG; ++r)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int h = 32 * mt + m;
-        f.a[r][mt][s] = __builtin_bit_cast(v8bf, st[r * kHeads * 16 + 16 * h + ((8 * g + s) ^ swz(h))]);
-      }
+    for (int s = 0; s < D / 16; ++s) {
+      const int h = 32 * mt + m;
+      f.a[mt][s] = __builtin_bit_cast(v8bf, st[16 * h + ((8 * g + s) ^ swz(h))]);
+    }
 }
 
 // max(x, 0) in one instruction: as signed integers, negative floats
@@ -406,11 +396,11 @@ __device__ __forceinline__ void wait_page_with_later(int later) {
   else wait_all_loads();
 }
 
-// Head weights of the group's rows as the accumulator layout needs them:
-// lane half g, M-tile mt, register v -> head 32 mt + 8 (v / 4) + 4 g + v % 4.
-template <int RG, int MT>
+// Head weights of a row as the accumulator layout needs them: lane half g,
+// M-tile mt, register v -> head 32 mt + 8 (v / 4) + 4 g + v % 4.
+template <int MT>
 struct WFrag {
-  float v[RG][MT][16];
+  float v[MT][16];
 };
 
 // Output of one row: a raw buffer over its L logits, so that stores of keys
@@ -431,10 +421,10 @@ __device__ __forceinline__ RowOut row_out(float* base, int L) {
 
 // Weighted ReLU head sum of one accumulator tile into four partial sums
 // (independent chains, so the FMAs do not wait on each other).
-template <int RG, int MT>
-__device__ __forceinline__ void head_sum(const v16f& acc, const WFrag<RG, MT>& wf, int r, int mt, float (&ps)[4]) {
+template <int MT>
+__device__ __forceinline__ void head_sum(const v16f& acc, const WFrag<MT>& wf, int mt, float (&ps)[4]) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) ps[v % 4] += wf.v[r][mt][v] * relu(acc[v]);
+  for (int v = 0; v < 16; ++v) ps[v % 4] += wf.v[mt][v] * relu(acc[v]);
 }
 
 // Logit of this lane's key from its four partial sums: add the other lane
@@ -449,7 +439,7 @@ __device__ __forceinline__ void finish_key(const float (&ps)[4], float key_scale
 
 // Raw scores of one row against 32-key tile nt of a raw page in LDS.
 template <int D, bool MX, int MT>
-__device__ __forceinline__ void tile_mfma_raw(const uint8_t* buf, int nt, const QFrag<D, 1, MT>& qf, v16f (&acc)[MT],
+__device__ __forceinline__ void tile_mfma_raw(const uint8_t* buf, int nt, const QFrag<D, MT>& qf, v16f (&acc)[MT],
                                               float& key_scale) {
   using Geo = Geometry<D, MX>;
   const int lane = lane_id();
@@ -462,17 +452,17 @@ __device__ __forceinline__ void tile_mfma_raw(const uint8_t* buf, int nt, const 
 #pragma unroll
   for (int s = 0; s < Geo::kKSteps; ++s)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[0][mt][s], bfr[s], acc[mt], 0, 0, 0);
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[mt][s], bfr[s], acc[mt], 0, 0, 0);
 }
 
 // Logits of one 32-key tile from its raw scores; `off` is the byte offset
 // of this lane's key in the row (out of range: nothing stored).
 template <int MT>
-__device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_scale, const WFrag<1, MT>& wf,
+__device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_scale, const WFrag<MT>& wf,
                                             const RowOut& out, int off) {
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) head_sum<1, MT>(acc[mt], wf, 0, mt, ps);
+  for (int mt = 0; mt < MT; ++mt) head_sum<MT>(acc[mt], wf, mt, ps);
   finish_key(ps, key_scale, out, (lane_id() >> 5) == 0 ? off : 0x7FFFFFF0);
 }
 
@@ -483,7 +473,7 @@ template <int D, bool MX>
 struct BlockShared {
   int page_prefix[kMaxGroups + 1];
   int req_tab[4][kMaxReqPrefill + 1];
-  float wbuf[kBlockRows][1][kMaxHeads];
+  float wbuf[kBlockRows][kMaxHeads];
   int misc[16];
   alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
   alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
@@ -559,7 +549,7 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
 // staged query load, or null.  Returns the row's key count.
 template <int D, int MT>
 __device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
-                                         float* wrow, QFrag<D, 1, MT>& qf, WFrag<1, MT>& wf, RowOut& out,
+                                         float* wrow, QFrag<D, MT>& qf, WFrag<MT>& wf, RowOut& out,
                                          uint8_t* stage) {
   const RowArgs& R = p.rows;
   const int lane = lane_id();
@@ -570,11 +560,11 @@ __device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_t
   const bool real = rl[0];
   // weights first: they land with (not after) the queries
   const float wv = p.w[static_cast<int64_t>(real ? qr[0] : 0) * p.heads + (lane < p.heads ? lane : 0)];
-  if constexpr (query_stage_bytes<D, 1, MT>() > 0) {
-    if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, 1, MT>(p, qr, stage, qf);
-    else load_query<D, 1, MT>(p, qr, qf);
+  if constexpr (query_stage_bytes<D, MT>() > 0) {
+    if (stage != nullptr && p.heads == 32 * MT) load_query_staged<D, MT>(p, qr[0], stage, qf);
+    else load_query<D, MT>(p, qr[0], qf);
   } else {
-    load_query<D, 1, MT>(p, qr, qf);
+    load_query<D, MT>(p, qr[0], qf);
   }
   wrow[lane] = (!real || lane >= p.heads) ? 0.0f : wv;
   out = row_out(p.logits + static_cast<int64_t>(gd.row0) * p.logits_stride + gd.col0, Lr);
@@ -585,10 +575,10 @@ __device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_t
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const float4 x = *reinterpret_cast<const float4*>(&wrow[32 * mt + 8 * i4 + hg]);
-      wf.v[0][mt][4 * i4 + 0] = x.x;
-      wf.v[0][mt][4 * i4 + 1] = x.y;
-      wf.v[0][mt][4 * i4 + 2] = x.z;
-      wf.v[0][mt][4 * i4 + 3] = x.w;
+      wf.v[mt][4 * i4 + 0] = x.x;
+      wf.v[mt][4 * i4 + 1] = x.y;
+      wf.v[mt][4 * i4 + 2] = x.z;
+      wf.v[mt][4 * i4 + 3] = x.w;
     }
   __builtin_amdgcn_wave_barrier();
   return __builtin_amdgcn_readfirstlane(Lr);
@@ -600,7 +590,7 @@ __device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_t
 template <int D, bool MX, int MT>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScoreParams p) {
   constexpr int kThreads = kDecodeWaves * kWave;
-  __shared__ ScoreShared<D, MX, 1, MT, kDecodeWaves> sm;
+  __shared__ ScoreShared<D, MX, MT, kDecodeWaves> sm;
   const RowArgs& R = p.rows;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -617,9 +607,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
 
-  float* wrow = sm.wbuf[wave][0];
-  WaveArea<D, MX, 1, MT>& area = sm.area[wave];
-  constexpr int NP = ring_pages<D, MX, 1, MT>();
+  float* wrow = sm.wbuf[wave];
+  WaveArea<D, MX, MT>& area = sm.area[wave];
+  constexpr int NP = ring_pages<D, MX, MT>();
   static_assert(NP >= 2 && NP <= 4, "ring of two to four pages");
   const uint32_t ring_lds = lds_addr(area.page[0]);  // page i of the ring at ring_lds + i * kPageBytes
 
@@ -644,8 +634,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
     // The first group's queries and weights are loaded together with the
     // ids and before any page is requested: waiting for them then never
     // waits for a page, and the first page can be scored as soon as it lands.
-    QFrag<D, 1, MT> qf;
-    WFrag<1, MT> wf;
+    QFrag<D, MT> qf;
+    WFrag<MT> wf;
     RowOut out;
     int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
     int row_len = setup_row<D, MT>(p, sm.req_tab, gs, wrow, qf, wf, out, area.stage);
@@ -739,7 +729,7 @@ __device__ __forceinline__ void decode_page_slice(const uint8_t* raw, v8bf* dec,
 // Raw scores of one row against 32-key tile nt of a decoded page (fp8 token
 // scales from the raw page).
 template <int D, bool MX, int MT>
-__device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, int nt, const QFrag<D, 1, MT>& qf,
+__device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, int nt, const QFrag<D, MT>& qf,
                                           v16f (&acc)[MT], float& key_scale) {
   constexpr int KS = D / 16;
   const int lane = lane_id();
@@ -750,7 +740,7 @@ __device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, i
   for (int s = 0; s < KS; ++s) {
     const v8bf b = dec[(nt * KS + s) * kWave + lane];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[0][mt][s], b, acc[mt], 0, 0, 0);
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[mt][s], b, acc[mt], 0, 0, 0);
   }
 }
 
@@ -758,8 +748,8 @@ __device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, i
 // output descriptor.
 template <int D, int MT>
 __device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
-                                                int wave, float (*wbuf)[kMaxHeads], QFrag<D, 1, MT>& qf,
-                                                WFrag<1, MT>& wf, RowOut (&out)[1]) {
+                                                int wave, float* wrow, QFrag<D, MT>& qf, WFrag<MT>& wf,
+                                                RowOut (&out)[1]) {
   const RowArgs& R = p.rows;
   const int lane = lane_id();
   int L[kBlockRows], ql[kBlockRows];
@@ -767,11 +757,11 @@ __device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int 
   const GroupDesc gd =
       describe_group<kBlockRows>(R, req_tab, g, group_request<kBlockRows>(R, req_tab, g), L, ql, rl);
   const bool exists = wave < gd.nrows;
-  const int qrow[1] = {exists ? ql[wave] : -1};
-  load_query<D, 1, MT>(p, qrow, qf);
-  float wv = p.w[static_cast<int64_t>(exists ? qrow[0] : 0) * p.heads + (lane < p.heads ? lane : 0)];
+  const int qrow = exists ? ql[wave] : -1;
+  load_query<D, MT>(p, qrow, qf);
+  float wv = p.w[static_cast<int64_t>(exists ? qrow : 0) * p.heads + (lane < p.heads ? lane : 0)];
   if (!exists || lane >= p.heads) wv = 0.0f;
-  wbuf[0][lane] = wv;
+  wrow[lane] = wv;
   out[0] = row_out(p.logits + static_cast<int64_t>(gd.row0 + wave) * p.logits_stride + gd.col0, exists ? L[wave] : 0);
   __builtin_amdgcn_wave_barrier();
   const int hg = 4 * (lane >> 5);
@@ -779,11 +769,11 @@ __device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int 
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 x = *reinterpret_cast<const float4*>(&wbuf[0][32 * mt + 8 * i4 + hg]);
-      wf.v[0][mt][4 * i4 + 0] = x.x;
-      wf.v[0][mt][4 * i4 + 1] = x.y;
-      wf.v[0][mt][4 * i4 + 2] = x.z;
-      wf.v[0][mt][4 * i4 + 3] = x.w;
+      const float4 x = *reinterpret_cast<const float4*>(&wrow[32 * mt + 8 * i4 + hg]);
+      wf.v[mt][4 * i4 + 0] = x.x;
+      wf.v[mt][4 * i4 + 1] = x.y;
+      wf.v[mt][4 * i4 + 2] = x.z;
+      wf.v[mt][4 * i4 + 3] = x.w;
     }
   __builtin_amdgcn_wave_barrier();
 }
@@ -833,8 +823,8 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
     return ok ? id : 0;
   };
 
-  QFrag<D, 1, MT> qf;
-  WFrag<1, MT> wf;
+  QFrag<D, MT> qf;
+  WFrag<MT> wf;
   RowOut out[1];
   int gs = group_of_page(sm.page_prefix, NG, j0);
   setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
