@@ -46,6 +46,9 @@ CASES = [
     # one long request among short ones: most workgroups get one or two pages,
     # and ranges start and end inside groups of every size
     ([5000, 70, 65, 1, 130, 64], [8, 8, 3, 1, 20, 64], 6000, 1 << 22, "fp8", 64, 128, 32),
+    # a chunk of fewer than 512 rows with rows past 32768 keys: the selector
+    # splits those rows over workgroups and merges them
+    ([40000, 300], [64, 16], 41000, 1 << 26, "fp8", 16, 64, 256),
 ]
 
 
