@@ -34,9 +34,6 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
-}
 // The same with a wave-uniform base in scalar registers and a per-lane byte
 // offset (global address sbase + voff; no immediate offset), so that a
 // page's address arithmetic runs on the scalar unit.

@@ -17,9 +17,10 @@
 // (2-4) pages in LDS filled by direct global->LDS loads
 // (global_load_lds_dwordx4, 1 KiB per instruction): while page j is scored
 // from one buffer, pages j+1 .. j+NP-1 are already in flight, and page j+NP
-// is requested as soon as page j's buffer is consumed.  No staging registers are used, and the waits are
-// explicit vmcnt counts (loads retire in order; every wait leaves exactly the
-// loads issued after the page it needs outstanding).
+// is requested as soon as page j's buffer is consumed.  No staging
+// registers are used, and the waits are explicit vmcnt counts (loads retire
+// in order; every wait leaves exactly the loads issued after the page it
+// needs outstanding).
 //
 // Per page (64 keys) a wave decodes its B fragments (32 keys per 32x32x16
 // MFMA) from LDS to bf16 and runs bf16 MFMAs against query fragments held in
@@ -749,7 +750,7 @@ __device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, i
 template <int D, int MT>
 __device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int (*req_tab)[kMaxReqPrefill + 1], int g,
                                                 int wave, float* wrow, QFrag<D, MT>& qf, WFrag<MT>& wf,
-                                                RowOut (&out)[1]) {
+                                                RowOut& out) {
   const RowArgs& R = p.rows;
   const int lane = lane_id();
   int L[kBlockRows], ql[kBlockRows];
@@ -762,7 +763,7 @@ __device__ __forceinline__ void setup_block_row(const ScoreParams& p, const int 
   float wv = p.w[static_cast<int64_t>(exists ? qrow : 0) * p.heads + (lane < p.heads ? lane : 0)];
   if (!exists || lane >= p.heads) wv = 0.0f;
   wrow[lane] = wv;
-  out[0] = row_out(p.logits + static_cast<int64_t>(gd.row0 + wave) * p.logits_stride + gd.col0, exists ? L[wave] : 0);
+  out = row_out(p.logits + static_cast<int64_t>(gd.row0 + wave) * p.logits_stride + gd.col0, exists ? L[wave] : 0);
   __builtin_amdgcn_wave_barrier();
   const int hg = 4 * (lane >> 5);
 #pragma unroll
@@ -825,7 +826,7 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
 
   QFrag<D, MT> qf;
   WFrag<MT> wf;
-  RowOut out[1];
+  RowOut out;
   int gs = group_of_page(sm.page_prefix, NG, j0);
   setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
   int g_first = sm.page_prefix[gs];
@@ -875,14 +876,14 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
       const uint8_t* raw = sm.ring[i % kRing];
       const int base = (j - g_first) * kPage * 4 + key_off;
       tile_mfma<D, MX, MT>(dec, raw, 0, qf, acc0, ks0);
-      tile_logits<MT>(acc1, ks1, wf, out[0], off1);
+      tile_logits<MT>(acc1, ks1, wf, out, off1);
       __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
       tile_mfma<D, MX, MT>(dec, raw, 1, qf, acc1, ks1);
-      tile_logits<MT>(acc0, ks0, wf, out[0], base);
+      tile_logits<MT>(acc0, ks0, wf, out, base);
       __builtin_amdgcn_sched_barrier(0);
       off1 = base + 32 * 4;
     }
-    tile_logits<MT>(acc1, ks1, wf, out[0], off1);  // the segment's last tile
+    tile_logits<MT>(acc1, ks1, wf, out, off1);  // the segment's last tile
     if (j >= j1) break;
     gs = advance_group(sm.page_prefix, gs, j);
     setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);

@@ -577,7 +577,7 @@ __device__ __forceinline__ void select_row_reg(const float* __restrict__ row, in
   __syncthreads();
   const int W = (L + 31) >> 5;
 
-  // 6. ordered emission: thread t owns bitmap words [t wpt, (t + 1) wpt)
+  // 5. ordered emission: thread t owns bitmap words [t wpt, (t + 1) wpt)
   const int wpt = (W + NT - 1) / NT;
   const int w0 = tid * wpt;
   const int w1 = (w0 + wpt < W) ? w0 + wpt : W;

@@ -22,8 +22,8 @@ struct TopkParams {
 // Key count L and logits column base of row r (DECODE grid row or PREFILL
 // chunk row); every thread of the workgroup gets the same values.
 template <int NT>
-__device__ __forceinline__ void row_window(const TopkParams& p, int r, int& L_out, int& col0_out, SelectShared<NT>& sm,
-                           int (&info)[2]) {
+__device__ __forceinline__ void row_window(const TopkParams& p, int r, int& L_out, int& col0_out,
+                                           SelectShared<NT>& sm, int (&info)[2]) {
   const RowArgs& R = p.rows;
   int L = 0, col0 = 0;
   if (R.kind == 0) {
