@@ -142,12 +142,17 @@ def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
 
 
 def load_traffic(per_launch_bytes: int):
+    """The scorer's measured HBM bytes per launch from the committed counter
+    profile, or None unless that profile was taken on the current kernel
+    source and on this workload (the same algorithmic bytes per launch)."""
     path = os.path.join(ROOT, "profiles", PROFILE_NAME + ".json")
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         prof = json.load(f)
     if prof.get("source_hash") != kernel_source_hash():
+        return None, prof
+    if prof.get("algorithmic_bytes_per_launch") != per_launch_bytes:
         return None, prof
     t = prof.get("traffic_bytes_per_launch")
     return t, prof

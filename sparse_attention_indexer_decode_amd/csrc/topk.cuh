@@ -80,8 +80,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 // Chunk c of a row holds its keys [c kRowCap, min(L, (c + 1) kRowCap)); the
 // chunk's own top-k holds every key of the row's top-k that lies in it (ties
 // go to the lower position inside a chunk as in the row).  Workgroup
-// (r, c) of topk_chunk_kernel selects chunk c into cand[r][c][0 .. k); a row
-// of at most kRowCap keys is finished there by its chunk 0.  The chunk also
+// c * rows + r of topk_chunk_kernel selects chunk c of row r into
+// cand[r][c][0 .. k); a row of at most kRowCap keys is finished there by
+// its chunk 0.  The chunk also
 // writes its candidates' logits and row positions, so that a row's
 // candidates lie in position order -- chunk by chunk, each chunk's list
 // ascending.  Then one workgroup per long row (topk_merge_kernel) selects k
@@ -91,8 +92,12 @@ template <int NT>
 __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   __shared__ SelectShared<NT> sm;
   __shared__ int info[2];
-  const int r = blockIdx.x / p.chunks;
-  const int c = blockIdx.x - r * p.chunks;
+  // chunk-major numbering: workgroup i runs on XCD i % 8, so the chunk-0
+  // workgroups (all the work of rows of at most kRowCap keys) are spread
+  // over every XCD by row, and are dispatched first
+  const int nr = gridDim.x / p.chunks;
+  const int c = blockIdx.x / nr;
+  const int r = blockIdx.x - c * nr;
   int L, col0;
   row_window<NT>(p, r, L, col0, sm, info);
   const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
