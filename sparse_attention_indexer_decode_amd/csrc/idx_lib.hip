@@ -221,10 +221,11 @@ int topk_chunks(const RowArgs& R) {
   return c <= kMaxTopkChunks ? static_cast<int>(c) : 0;
 }
 
-// Workspace bytes of the chunk candidates (three [rows][chunks][k] arrays).
+// Workspace bytes of the chunk candidates (two [rows][chunks][k] arrays:
+// logits and row positions).
 size_t topk_chunk_bytes(const RowArgs& R, int k) {
   const int c = topk_chunks(R);
-  return c ? align_up(3 * sizeof(int32_t) * static_cast<size_t>(R.num_rows) * c * k, 256) : 0;
+  return c ? align_up(2 * sizeof(int32_t) * static_cast<size_t>(R.num_rows) * c * k, 256) : 0;
 }
 
 idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, int k, int32_t* out,
@@ -239,12 +240,13 @@ idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, in
   if (nc > 0) {
     const size_t n = static_cast<size_t>(R.num_rows) * nc * k;
     p.chunks = nc;
-    p.cand = static_cast<int32_t*>(chunk_ws);
-    p.cand_val = reinterpret_cast<float*>(p.cand + n);
+    p.cand_val = static_cast<float*>(chunk_ws);
     p.cand_pos = reinterpret_cast<int32_t*>(p.cand_val + n);
-    // unused dynamic LDS that keeps two of these workgroups off one CU (the
-    // launch has at most a few hundred; doubling up would halve their speed)
+    // dynamic LDS: the k selected positions of a chunk or a merge, sized so
+    // that two of these workgroups never share a CU (the launch has at most
+    // a few hundred; doubling up would halve their speed)
     constexpr unsigned kOneWgPerCu = 48 * 1024;
+    static_assert(kOneWgPerCu >= sizeof(int32_t) * kMaxK, "k positions must fit the dynamic LDS");
     hipLaunchKernelGGL(topk_chunk_kernel<kTopkThreads>, dim3(R.num_rows * nc), dim3(kTopkThreads), kOneWgPerCu, s, p);
     hipLaunchKernelGGL(topk_merge_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), kOneWgPerCu, s, p);
     return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");

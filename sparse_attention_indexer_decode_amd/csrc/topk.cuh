@@ -14,7 +14,6 @@ struct TopkParams {
   int32_t* out;
   // long rows split over workgroups (topk_chunk_kernel / topk_merge_kernel)
   int32_t chunks;     // chunk slots per row (ceil(max_keys / kRowCap))
-  int32_t* cand;      // [rows][chunks][k] chunk top-k positions
   float* cand_val;    // [rows][chunks * k] candidate logits in position order
   int32_t* cand_pos;  // [rows][chunks * k] their positions in the row
 };
@@ -80,8 +79,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 // Chunk c of a row holds its keys [c kRowCap, min(L, (c + 1) kRowCap)); the
 // chunk's own top-k holds every key of the row's top-k that lies in it (ties
 // go to the lower position inside a chunk as in the row).  Workgroup
-// c * rows + r of topk_chunk_kernel selects chunk c of row r into
-// cand[r][c][0 .. k); a row of at most kRowCap keys is finished there by
+// c * rows + r of topk_chunk_kernel selects k positions of chunk c of row r
+// (into dynamic LDS); a row of at most kRowCap keys is finished there by
 // its chunk 0.  The chunk also
 // writes its candidates' logits and row positions, so that a row's
 // candidates lie in position order -- chunk by chunk, each chunk's list
@@ -109,14 +108,16 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   if (lo >= L) return;
   const int Lc = L - lo < kRowCap ? L - lo : kRowCap;
   const int64_t slot = (static_cast<int64_t>(r) * p.chunks + c) * p.k;
-  select_row<NT>(row + lo, Lc, p.k, p.cand + slot, sm);
+  // the chunk's k selected positions go to the launch's dynamic LDS
+  extern __shared__ int sel_pos[];
+  select_row<NT>(row + lo, Lc, p.k, sel_pos, sm);
   // the candidates' logits and row positions, laid out for the merge while
   // the chunk is still in cache (every chunk but the last has more than k
   // keys, so the row's candidates are contiguous)
   __syncthreads();  // the selected positions are visible to every thread
   const int m = Lc < p.k ? Lc : p.k;
   for (int j = threadIdx.x; j < m; j += NT) {
-    const int t = lo + p.cand[slot + j];
+    const int t = lo + sel_pos[j];
     p.cand_pos[slot + j] = t;
     p.cand_val[slot + j] = row[t];
   }
@@ -140,16 +141,15 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   const float* val = p.cand_val + base;
   const int32_t* pos = p.cand_pos + base;
   int32_t* out = p.out + static_cast<int64_t>(r) * k;
-  // n > k: k candidate indices, ascending; the register path sized to n
-  // (its passes cost the keys per thread it is built for, not n)
-  if (n <= 8 * NT) select_row_reg<NT, 8>(val, n, k, out, sm);
-  else if (n <= 16 * NT) select_row_reg<NT, 16>(val, n, k, out, sm);
-  else select_row_reg<NT, kRowCap / NT>(val, n, k, out, sm);
+  // n > k: k candidate indices, ascending, into the launch's dynamic LDS;
+  // the register path sized to n (its passes cost the keys per thread it
+  // is built for, not n)
+  extern __shared__ int sel_idx[];
+  if (n <= 8 * NT) select_row_reg<NT, 8>(val, n, k, sel_idx, sm);
+  else if (n <= 16 * NT) select_row_reg<NT, 16>(val, n, k, sel_idx, sm);
+  else select_row_reg<NT, kRowCap / NT>(val, n, k, sel_idx, sm);
   __syncthreads();
-  for (int j = threadIdx.x; j < k; j += NT) {
-    const int ci = out[j];
-    out[j] = pos[ci];
-  }
+  for (int j = threadIdx.x; j < k; j += NT) out[j] = pos[sel_idx[j]];
 }
 
 }  // namespace idx

@@ -176,11 +176,11 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(B.IDX_OP_LOGITS, ctypes.byref(c), ctypes.byref(r), 64, 0) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, 16) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 99, 16) == 0
-    # long rows in a small batch: chunk candidates (3 x rows x chunks x k int32)
+    # long rows in a small batch: chunk candidates (2 x rows x chunks x k 4-byte values)
     rl = _rows(num_req=64, max_seq_len=131072, bt_width=2048, bt_stride=2048)
-    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 2048) == 256 + 3 * 4 * 64 * 4 * 2048
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 2048) == 256 + 2 * 4 * 64 * 4 * 2048
     assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(rl), 64, 2048) == \
-        256 + 64 * 131072 * 4 + 3 * 4 * 64 * 4 * 2048
+        256 + 64 * 131072 * 4 + 2 * 4 * 64 * 4 * 2048
     # many rows take the one-workgroup-per-row streaming path: no candidates
     rm = _rows(num_req=600, max_seq_len=131072, bt_width=2048)
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rm), 0, 2048) == 256
