@@ -297,3 +297,40 @@ def test_topk_long_rows_split_over_workgroups(k):
     for r, v in enumerate(rows):
         exp = oracle.topk.topk_row(v.astype(np.float64), len(v), k)
         assert np.array_equal(o[r], exp), f"row {r} (L={len(v)}, k={k})"
+
+
+@pytest.mark.parametrize("k", [1, 100, 2048, 4096])
+def test_topk_split_random_mix(k):
+    """A seeded mix of short rows and rows split over workgroups (odd row
+    count, lengths at and around the 32768-key chunk boundaries, tied and
+    untied values): every row bit-exact against the oracle."""
+    rng = np.random.default_rng(4000 + k)
+    fixed = [32768, 32769, 65536, 65537, 98304, 131072, 1, k, k + 1]
+    lens = fixed + [int(x) for x in rng.integers(1, 32769, size=10)] + \
+        [int(x) for x in rng.integers(32769, 131073, size=18)]
+    rows = []
+    for i, L in enumerate(lens):
+        if i % 3 == 0:
+            v = (np.round(rng.standard_normal(L) * 4) / 4).astype(np.float32)   # many ties
+        else:
+            v = rng.standard_normal(L).astype(np.float32)
+        rows.append(v)
+    R = len(lens)
+    assert R % 8 != 0
+    stride = max(lens) + 1
+    buf = np.full((R, stride), np.nan, dtype=np.float32)
+    for r, v in enumerate(rows):
+        buf[r, : len(v)] = v
+    d = torch.device("cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device=d)
+    bt = torch.zeros((R, 1), dtype=torch.int32, device=d)
+    rows_d = idx.Rows.decode(bt, seq, max(lens))
+    out = torch.full((R, k), -7, dtype=torch.int32, device=d)
+    ws = topk_workspace(rows_d, k, d)
+    assert ws.numel() > 256                 # the split path is taken
+    print(f"split mix k={k}: {R} rows, lengths {min(lens)}..{max(lens)}", flush=True)
+    idx.idx_topk(torch.from_numpy(buf).to(d), rows_d, k, out, ws)
+    got = out.cpu().numpy()
+    for r, v in enumerate(rows):
+        exp = oracle.topk.topk_row(v.astype(np.float64), lens[r], k)
+        assert np.array_equal(got[r], exp), f"row {r} (L={lens[r]}, k={k}) differs"
