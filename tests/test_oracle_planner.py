@@ -59,3 +59,46 @@ def test_coverage_and_budget_random():
                 assert N <= ws
             if q1 - q0 > 1 or re - rb > 1:
                 assert (q1 - q0) * N * 4 <= budget or N == 0
+
+
+def test_chunk_end_is_largest_fitting_brute_force():
+    """Rule 1 by enumeration: every chunk [s, e) of several requests fits
+    both budgets and adding request e would break one; a one-request chunk
+    either fits or no chunk starting there fits.  Slices cover the chunk's
+    query tokens in pieces of max(1, budget/4 // N)."""
+    rng = np.random.default_rng(21)
+    for _ in range(400):
+        n = int(rng.integers(1, 9))
+        seq = rng.integers(0, 120, size=n)
+        ql = np.minimum(rng.integers(0, 40, size=n), seq)
+        ws = int(rng.integers(1, 300))
+        budget = int(rng.integers(4, 40000))
+        elems = budget // 4
+
+        def fits(s, e):
+            N = sum(int(x) for x in seq[s:e])
+            M = sum(int(x) for x in ql[s:e])
+            return N <= ws and M * N <= elems
+
+        chunks = planner.split_chunks(seq, ql, ws, budget)
+        # expected boundaries: from each start, the largest end that fits
+        # (enumerating every end), else the lone request; chunks without
+        # query tokens produce no slice
+        expect = []
+        s = 0
+        while s < n:
+            ends = [e for e in range(s + 1, n + 1) if fits(s, e)]
+            e = max(ends) if ends else s + 1
+            if sum(int(x) for x in ql[s:e]) > 0:
+                expect.append((s, e))
+            s = e
+        got = []
+        for rb, re, q0, q1 in chunks:
+            if not got or got[-1] != (rb, re):
+                got.append((rb, re))
+        assert got == expect
+        for rb, re, q0, q1 in chunks:
+            N = sum(int(x) for x in seq[rb:re])
+            M = sum(int(x) for x in ql[rb:re])
+            width = max(1, elems // N) if N else M
+            assert q0 % width == 0 and q1 == min(q0 + width, M)

@@ -26,13 +26,14 @@ def test_grid_rows_e4():
 
 
 def test_uniform_grid_is_token_rows():
-    # full requests: both readings coincide with token_rows (mono runner page)
-    seq = [5, 100, 64, 65]
-    for q in (1, 2, 3):
-        L = rows.decode_lengths(seq, None, q)
-        assert L.tolist() == rows.token_rows(seq, q).tolist()
-        # and with the native-path formula seq - next_n + j + 1
-        assert L.tolist() == [s - q + j + 1 for s in seq for j in range(q)]
+    """Full requests (decode_len == next_n): the grid lengths are the mono
+    runner page's token_rows and the DeepSeek-V3.2 page's native 2-D
+    lengths, written out by hand here (seq 5 and 100 at next_n 1, 2, 3)."""
+    seq = [5, 100]
+    hand = {1: [5, 100], 2: [4, 5, 99, 100], 3: [3, 4, 5, 98, 99, 100]}
+    for q, exp in hand.items():
+        assert rows.decode_lengths(seq, None, q).tolist() == exp
+        assert rows.token_rows(seq, q).tolist() == exp
 
 
 def test_packed_mapping_brute_force():
