@@ -62,7 +62,7 @@ typedef int32_t idx_status;
 
 /* Bits of the device status word (first 4 bytes of a workspace). */
 #define IDX_DEV_BAD_PAGE 1u
-#define IDX_DEV_BAD_SLOT 2u  /* idx_cache_write: a slot at or past num_pages * 64 */
+#define IDX_DEV_BAD_SLOT 2u  /* idx_cache_write: a slot at or past num_pages * page_size */
 
 /*
  * Paged index cache (the `(num_blocks, block_size, head_size)` allocation of
@@ -160,12 +160,18 @@ int64_t idx_num_rows(const idx_rows* rows);
 #define IDX_OP_CACHE_WRITE 3
 
 /*
- * Bytes of device workspace `op` needs for these arguments (the caller
- * allocates it; 256-byte aligned).  Its first 256 bytes hold the device
- * status word (see idx_read_device_status), which must be zero before the
- * first use; nothing else needs clearing, so a workspace can be reused and
- * calls on it captured in a HIP graph.  Calls that share a workspace must
- * not overlap.  Returns 0 when the arguments are invalid.
+ * Bytes of device workspace `op` needs for these arguments.  The caller
+ * allocates it (256-byte aligned) once and passes it to every call, the way
+ * the DeepSeek-V3.2 indexer page's metadata builder preallocates its
+ * persistent buffers at fixed addresses so that captured CUDA graphs
+ * (UNIFORM_BATCH) can replay over them, and sizes its prefill gather
+ * workspace from the model's maximum length (get_max_prefill_buffer_size).
+ * Its first 256 bytes hold the device status word (see
+ * idx_read_device_status), which must be zero before the first use; nothing
+ * else needs clearing, so a workspace can be reused and calls on it
+ * captured in a HIP graph.  Calls that share a workspace must not overlap.
+ * Returns 0 when the arguments are invalid (for IDX_OP_TOPK and
+ * IDX_OP_DECODE_TOPK this includes k outside 1..4096).
  */
 size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* rows,
                            int32_t heads, int32_t k);
@@ -189,7 +195,11 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Top-k of rows of logits: out[r * k .. r * k + k) receives, in ascending
+ * Top-k of rows of logits (the top-k kernels of the DeepSeek-V3.2 indexer
+ * page, which take the per-token lengths of DeepSeekV32IndexerDecodeMetadata
+ * -- one per row, 1-D or the 2-D next_n grid -- and the exact causal fill of
+ * _fill_short_decode_causal_indices on the glm5next sparse_indexer page,
+ * applied per row): out[r * k .. r * k + k) receives, in ascending
  * order, the k key positions t < L(r) with the largest logits[r, col0 + t]
  * (col0 = 0 for DECODE, ks for PREFILL), ties going to the lower position,
  * -1 padded.  Rows with L <= k get 0..L-1 (exact causal fill); padded rows
@@ -226,8 +236,9 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
  * reads.  The int64 per-token slot mapping is the one the DeepSeek-V3.2
  * indexer page's metadata carries (slot_mapping and its compressed variant)
  * and the MiniMax-M3 mono runner page documents for its page slots: token t
- * goes to row slot % 64 of page slot / 64; a negative slot (a padding token)
- * is skipped.  The row layouts are those of idx_cache (the glm5next page's
+ * goes to row slot % page_size of page slot / page_size (64-token pages, or
+ * 256-token pages of the compressed cache); a negative slot (a padding
+ * token) is skipped.  The row layouts are those of idx_cache (the glm5next page's
  * _gather_workspace_shapes).  The pages do not print the quantiser; this one
  * follows the per-token absmax / OCP MX block-scale reading:
  *   FP8_E4M3  scale = amax/448 as an fp32 division (1 for an all-zero row),
@@ -246,8 +257,8 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
  *   slot_mapping  device int64 [num_tokens], 8-byte aligned; slots must be
  *                 distinct (two tokens on one slot race)
  *   num_tokens    >= 0 (0 enqueues nothing)
- * A slot at or past num_pages * 64 is skipped and sets IDX_DEV_BAD_SLOT in
- * the workspace status word.  Workspace: idx_workspace_bytes(
+ * A slot at or past num_pages * page_size is skipped and sets
+ * IDX_DEV_BAD_SLOT in the workspace status word.  Workspace: idx_workspace_bytes(
  * IDX_OP_CACHE_WRITE, cache, NULL, 0, 0) bytes (the status word only).
  */
 idx_status idx_cache_write(const idx_cache* cache, const uint16_t* k, int64_t k_stride,
@@ -277,7 +288,15 @@ idx_status idx_prefill_chunks(const int32_t* seq_lens, const int32_t* query_lens
  */
 idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream);
 
-/* Static description of a status code. */
+/*
+ * Static description of a status code.  The codes follow how the pages'
+ * callers refuse work: the MiniMax-M3 mono runner page raises
+ * MonoUnsupported for a configuration its kernels were not built for (here
+ * IDX_EUNSUPPORTED), and the DeepSeek-V3.2 indexer backend asserts its
+ * supported head sizes, block sizes and single KV head before building
+ * metadata (here IDX_EINVAL / IDX_EUNSUPPORTED, returned before anything is
+ * enqueued).  Unknown codes give "unknown status".
+ */
 const char* idx_status_string(idx_status s);
 
 /*

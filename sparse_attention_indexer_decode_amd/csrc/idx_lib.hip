@@ -286,7 +286,7 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
   }
   if (op == IDX_OP_TOPK) {
     if (check_rows(rows, false, R) != IDX_OK) return 0;
-    if (k < 1 || k > kMaxK) return kStatusBytes;
+    if (k < 1 || k > kMaxK) return 0;
     return kStatusBytes + topk_chunk_bytes(R, k);
   }
   CacheArgs C;

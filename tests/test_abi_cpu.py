@@ -176,6 +176,11 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(B.IDX_OP_LOGITS, ctypes.byref(c), ctypes.byref(r), 64, 0) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, 16) == 256
     assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 99, 16) == 0
+    # k outside 1..4096: invalid for both selecting operations
+    for k in (0, -3, 4097):
+        assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, k) == 0
+        assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 64, k) == 0
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, 4096) == 256
     # long rows in a small batch: chunk candidates (2 x rows x chunks x k 4-byte values)
     rl = _rows(num_req=64, max_seq_len=131072, bt_width=2048, bt_stride=2048)
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 2048) == 256 + 2 * 4 * 64 * 4 * 2048

@@ -52,13 +52,17 @@ def test_cache_write_bitexact(case):
     assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
 
 
-def test_cache_write_bad_slots_skipped_and_flagged():
-    x = cache_write_inputs(seed=77, tokens=400, head_dim=128, fmt="fp8", num_pages=10)
+@pytest.mark.parametrize("ps", [64, 256])
+def test_cache_write_bad_slots_skipped_and_flagged(ps):
+    """Slots at or past num_pages * page_size are skipped and flagged; the
+    last slot of the pool (num_pages * page_size - 1) is written."""
+    x = cache_write_inputs(seed=77, tokens=400, head_dim=128, fmt="fp8", num_pages=10, page_size=ps)
     slots = x.slots.copy()
-    cap = 10 * 64
-    slots[[3, 50, 399]] = [cap, cap + 12345, 1 << 40]
+    cap = 10 * ps
+    slots[slots == cap - 1] = -1
+    slots[[3, 50, 399, 7]] = [cap, cap + 12345, 1 << 40, cap - 1]
     got, status = _run(x, slots)
-    ref, bad = oracle.cache_write.write(x.cache, x.k_bits[:, :128], slots, fmt="fp8", page_size=64,
+    ref, bad = oracle.cache_write.write(x.cache, x.k_bits[:, :128], slots, fmt="fp8", page_size=ps,
                                         page_bytes=x.page_bytes)
     assert bad and status == idx.IDX_DEV_BAD_SLOT
     assert np.array_equal(got, ref)
