@@ -70,8 +70,41 @@ def test_c1_tiny_decode():
     out, _ = dev.decode_topk()
     L, _ = oracle.pipeline.decode_row_info(wl)
     check_topk_e2e(out, ref, L, wl.topk, label="C1")
-    # the fused path on the oracle's own logits would pick the oracle's set exactly
-    assert out.shape == (1, 64)
+    # the fused path selects exactly what the oracle's selection picks from
+    # the GPU's own logits (same fp32 values, so bit-exact)
+    exp = oracle.topk.topk_row(got[0, : L[0]].astype(np.float64), int(L[0]), wl.topk)
+    assert out.shape == (1, 64) and np.array_equal(out[0], exp)
+    # and idx_topk on the oracle's fp32-rounded logits is the oracle's selection
+    buf = fp32_rows(ref, 1, got.shape[1])
+    rows = dev.decode_rows()
+    o2 = torch.full((1, wl.topk), -7, dtype=torch.int32, device=dev.device)
+    idx.idx_topk(torch.from_numpy(buf).to(dev.device), rows, wl.topk, o2, topk_workspace(rows, wl.topk))
+    exp2 = oracle.topk.topk_row(buf[0, : L[0]].astype(np.float64), int(L[0]), wl.topk)
+    assert np.array_equal(o2.cpu().numpy()[0], exp2)
+
+
+SEQS_LONG = [5000, 33000, 70001, 140001]
+LONG_SHAPES = [("fp8", 128, 64, 1, False), ("fp8", 128, 64, 2, True), ("mxfp4", 128, 64, 1, False),
+               ("fp8", 64, 16, 3, False)]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_decode_long_rows(shape):
+    """Rows from 5000 to 140001 keys (past the selector's 32768-key register
+    rows and its 131072-position bitmap), k = 2048, next_n 1..3."""
+    fmt, D, H, nn, packed = shape
+    rng = np.random.default_rng(300 + LONG_SHAPES.index(shape))
+    dl = None if nn == 1 else rng.integers(1, nn + 1, size=len(SEQS_LONG)).astype(np.int32)
+    wl = build_decode(seed=300 + LONG_SHAPES.index(shape), seq_lens=SEQS_LONG, heads=H, head_dim=D, topk=2048,
+                      fmt=fmt, next_n=nn, decode_lens=dl, q_packed=packed, name=f"long-{fmt}-D{D}-H{H}-n{nn}")
+    print(f"case {wl.name} packed={packed} seqs={SEQS_LONG} dl={dl}", flush=True)
+    dev = Dev(wl)
+    ref = oracle.pipeline.decode_logits(wl)
+    got, _ = dev.logits_decode()
+    check_logits(got, {r: v for r, v in ref.items() if len(v)}, label=wl.name)
+    L, _ = oracle.pipeline.decode_row_info(wl)
+    out, _ = dev.decode_topk()
+    check_topk_e2e(out, ref, L, wl.topk, label=wl.name)
 
 
 def _topk_rows(k):
