@@ -231,6 +231,28 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * idx_decode_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same output, with the row logits and chunk
+ * candidates kept in a static device array of the library instead of a
+ * caller workspace.  That array is 160 MiB (enough for 256 grid rows of
+ * 131072 keys at k = 2048); arguments that would need more
+ * (idx_workspace_bytes(IDX_OP_DECODE_TOPK, ...) > 160 MiB) return
+ * IDX_ENOSPC before anything is enqueued.  Each GPU the library runs on
+ * holds its own copy from the first call on it until the process ends, and
+ * every call on that GPU shares it: calls that overlap on one GPU (two
+ * streams, two threads) race.  Nothing is allocated and nothing needs
+ * clearing between calls.
+ *   status  optional device uint32 (4-byte aligned) that receives the
+ *           IDX_DEV_* bits of this call OR-ed in (the caller zeroes it);
+ *           NULL: the bits are dropped
+ * Other arguments and the output as idx_decode_topk.
+ */
+idx_status idx_decode_topk_noalloc(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
+                                   const float* w, int32_t heads, int32_t k, int32_t* out, uint32_t* status,
+                                   void* stream);
+
+/*
  * Index-cache write: quantise new key tokens and store each token's row in
  * the paged cache at its slot, the step that fills the cache the scorer
  * reads.  The int64 per-token slot mapping is the one the DeepSeek-V3.2

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     IDX_DEV_BAD_SLOT,
     idx_cache_write,
     idx_decode_topk,
+    idx_decode_topk_noalloc,
     idx_logits_paged,
     idx_prefill_chunks,
     idx_read_device_status,

@@ -31,6 +31,7 @@ EXPORTED = (
     "idx_logits_paged",
     "idx_topk",
     "idx_decode_topk",
+    "idx_decode_topk_noalloc",
     "idx_cache_write",
     "idx_prefill_chunks",
     "idx_read_device_status",
@@ -91,6 +92,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.idx_decode_topk.argtypes = [POINTER(IdxCache), POINTER(IdxRows), c_void_p, c_void_p, c_int32,
                                     c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.idx_decode_topk.restype = c_int32
+    lib.idx_decode_topk_noalloc.argtypes = [POINTER(IdxCache), POINTER(IdxRows), c_void_p, c_void_p, c_int32,
+                                            c_int32, c_void_p, c_void_p, c_void_p]
+    lib.idx_decode_topk_noalloc.restype = c_int32
     lib.idx_cache_write.argtypes = [POINTER(IdxCache), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t,
                                     c_void_p]
     lib.idx_cache_write.restype = c_int32
@@ -219,6 +223,18 @@ def idx_decode_topk(cache: Cache, rows: Rows, q: torch.Tensor, w: torch.Tensor, 
     _check("idx_decode_topk", load().idx_decode_topk(
         ctypes.byref(cache.c), ctypes.byref(rows.c), q.data_ptr(), w.data_ptr(), q.shape[1], k,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def idx_decode_topk_noalloc(cache: Cache, rows: Rows, q: torch.Tensor, w: torch.Tensor, k: int,
+                            out: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
+    """idx_decode_topk without a workspace (the library's static scratch);
+    status: optional int32/uint32 device tensor of one element."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and w.dtype == torch.float32 and w.is_contiguous()
+    assert out.dtype == torch.int32 and out.is_contiguous()
+    assert status is None or (status.numel() >= 1 and status.element_size() == 4)
+    _check("idx_decode_topk_noalloc", load().idx_decode_topk_noalloc(
+        ctypes.byref(cache.c), ctypes.byref(rows.c), q.data_ptr(), w.data_ptr(), q.shape[1], k,
+        out.data_ptr(), _ptr(status), _stream(stream)))
 
 
 def idx_cache_write(cache: Cache, k: torch.Tensor, slot_mapping: torch.Tensor, workspace: torch.Tensor,

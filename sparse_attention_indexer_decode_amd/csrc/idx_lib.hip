@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/idx.h"
@@ -11,8 +12,17 @@
 #include "score.cuh"
 #include "topk.cuh"
 
+// Scratch of idx_decode_topk_noalloc: the row logits and long rows' chunk
+// candidates of one decode batch, in place of a caller workspace.  Each GPU
+// that runs the library holds its own copy until the process ends; calls on
+// one GPU share it (and race if they overlap).
+constexpr size_t kStaticScratchBytes = size_t{160} << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace idx {
 namespace {
+
+constexpr int kMaxDevices = 64;
 
 thread_local const char* g_last_error = "";
 
@@ -268,6 +278,65 @@ idx_status check_ws(void* ws, size_t have, size_t need) {
   return IDX_OK;
 }
 
+// Argument checks shared by the two decode top-k entry points.
+idx_status check_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q, const float* w,
+                             int heads, int k, const int32_t* out, CacheArgs& C, RowArgs& R) {
+  idx_status st = check_cache(cache, C);
+  if (st != IDX_OK) return st;
+  if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
+  if (R.kind != IDX_ROWS_DECODE) return fail(IDX_EINVAL, "idx_decode_topk takes DECODE rows");
+  if ((st = check_table(rows, R, C)) != IDX_OK) return st;
+  if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
+  if (!out) return fail(IDX_EINVAL, "out is null");
+  if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
+  if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
+  if (group_bound(R, pick_rg(R)) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
+  return IDX_OK;
+}
+
+// Scorer into the scratch's row logits (after its 256-byte header), then
+// top-k of each row (the kernel boundary orders the two); long rows' chunk
+// candidates follow the row logits.
+idx_status run_decode_topk(const CacheArgs& C, const RowArgs& R, const uint16_t* q, const float* w, int heads,
+                           int k, int32_t* out, uint8_t* ws, int32_t* header, hipStream_t s) {
+  float* logits = reinterpret_cast<float*>(ws + scratch_offset());
+  if (R.max_keys > 0) {
+    const int rg = pick_rg(R);
+    ScoreParams p{};
+    p.cache = C;
+    p.rows = R;
+    p.q = q;
+    p.w = w;
+    p.heads = heads;
+    p.logits = logits;
+    p.logits_stride = scratch_stride(R);
+    p.header = header;
+    p.num_groups = static_cast<int32_t>(group_bound(R, rg));
+    if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
+  }
+  return launch_topk(logits, scratch_stride(R), R, k, out, ws + decode_ws_bytes(R), s);
+}
+
+// This device's address of the static scratch (looked up once per device,
+// with that device current; the array's host-side name is not a device
+// address).
+idx_status static_scratch(uint8_t*& out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(IDX_EHIP, "hipGetDevice failed");
+  if (dev >= kMaxDevices) return fail(IDX_EUNSUPPORTED, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return fail(IDX_EHIP, "hipGetSymbolAddress of the static scratch failed");
+    addr[dev] = p;
+  }
+  out = static_cast<uint8_t*>(addr[dev]);
+  return IDX_OK;
+}
+
 }  // namespace
 }  // namespace idx
 
@@ -385,38 +454,32 @@ idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const u
                            size_t workspace_bytes, void* stream) {
   CacheArgs C;
   RowArgs R;
-  idx_status st = check_cache(cache, C);
+  idx_status st = check_decode_topk(cache, rows, q, w, heads, k, out, C, R);
   if (st != IDX_OK) return st;
-  if ((st = check_rows(rows, true, R)) != IDX_OK) return st;
-  if (R.kind != IDX_ROWS_DECODE) return fail(IDX_EINVAL, "idx_decode_topk takes DECODE rows");
-  if ((st = check_table(rows, R, C)) != IDX_OK) return st;
-  if ((st = check_queries(q, w, heads)) != IDX_OK) return st;
-  if (!out) return fail(IDX_EINVAL, "out is null");
-  if (k < 1) return fail(IDX_EINVAL, "k must be >= 1");
-  if (k > kMaxK) return fail(IDX_EUNSUPPORTED, "k must be <= 4096");
-  const int rg = pick_rg(R);
-  if (group_bound(R, rg) > kMaxGroups) return fail(IDX_EUNSUPPORTED, "too many row groups in one launch (limit 2048)");
   if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R) + topk_chunk_bytes(R, k))) != IDX_OK) return st;
   if (R.num_rows == 0) return IDX_OK;
-  // scorer into the workspace's row logits, then top-k of each row (the
-  // kernel boundary orders the two)
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* logits = reinterpret_cast<float*>(ws + scratch_offset());
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (R.max_keys > 0) {
-    ScoreParams p{};
-    p.cache = C;
-    p.rows = R;
-    p.q = q;
-    p.w = w;
-    p.heads = heads;
-    p.logits = logits;
-    p.logits_stride = scratch_stride(R);
-    p.header = reinterpret_cast<int32_t*>(ws);
-    p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-    if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
-  }
-  return launch_topk(logits, scratch_stride(R), R, k, out, ws + decode_ws_bytes(R), s);
+  return run_decode_topk(C, R, q, w, heads, k, out, ws, reinterpret_cast<int32_t*>(ws),
+                         static_cast<hipStream_t>(stream));
+}
+
+idx_status idx_decode_topk_noalloc(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
+                                   const float* w, int32_t heads, int32_t k, int32_t* out, uint32_t* status,
+                                   void* stream) {
+  CacheArgs C;
+  RowArgs R;
+  idx_status st = check_decode_topk(cache, rows, q, w, heads, k, out, C, R);
+  if (st != IDX_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(status) & 3) != 0) return fail(IDX_EINVAL, "status must be 4-byte aligned");
+  if (decode_ws_bytes(R) + topk_chunk_bytes(R, k) > kStaticScratchBytes)
+    return fail(IDX_ENOSPC, "rows need more than the 160 MiB static scratch (use idx_decode_topk with a workspace)");
+  if (R.num_rows == 0) return IDX_OK;
+  uint8_t* ws = nullptr;
+  if ((st = static_scratch(ws)) != IDX_OK) return st;
+  // the status bits go to the caller's word, or to the scratch header when
+  // there is none (nobody reads that one, so it needs no clearing)
+  int32_t* header = status ? reinterpret_cast<int32_t*>(status) : reinterpret_cast<int32_t*>(ws);
+  return run_decode_topk(C, R, q, w, heads, k, out, ws, header, static_cast<hipStream_t>(stream));
 }
 
 idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream) {

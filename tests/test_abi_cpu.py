@@ -231,3 +231,22 @@ def test_compressed_cache_validation(lib):
     # the decode logits stride has to hold max_seq_len / ratio keys
     assert _logits(lib, _cache(), _rows(max_seq_len=400, compress_ratio=4), stride=99) == E
     assert b"compress_ratio" in lib.idx_last_error()
+
+
+def test_noalloc_host_checks(lib):
+    """idx_decode_topk_noalloc: argument checks and the static-scratch limit
+    are decided on the host before anything is enqueued."""
+    E, S = B.IDX_EINVAL, B.IDX_ENOSPC
+    c = _cache()
+    big = _rows(num_req=400, max_seq_len=131072, bt_width=2048, bt_stride=2048)
+    assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(big), FAKE, FAKE, 64, 2048, FAKE, None,
+                                       None) == S
+    assert b"static scratch" in lib.idx_last_error()
+    r = _rows()
+    assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, 64, 16, None, None, None) == E
+    assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, 64, 0, FAKE, None, None) == E
+    assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, 64, 16, FAKE, FAKE + 2,
+                                       None) == E
+    empty = _rows(num_req=0)
+    assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(empty), FAKE, FAKE, 64, 16, FAKE, None,
+                                       None) == B.IDX_OK
