@@ -75,7 +75,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _LIB
     if _LIB is not None and path is None:
         return _LIB
-    p = path or LIB_PATH
+    # IDX_LIB_PATH selects another build of the same library (the host
+    # sanitizer build of the CPU tests)
+    p = path or os.environ.get("IDX_LIB_PATH") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"libidx.so not built at {p}; run __graft_entry__.build()")
     lib = ctypes.CDLL(p)
