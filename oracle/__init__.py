@@ -24,4 +24,4 @@ rationals, hand-worked examples, the pages' own worked example); see the
 module docstrings for which pin covers what.
 """
 
-from . import formats, rows, cache, cache_write, score, topk, planner, pipeline  # noqa: F401
+from . import formats, rows, cache, cache_write, score, topk, pool, planner, pipeline  # noqa: F401

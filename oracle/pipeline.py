@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import cache, rows, score, topk
+from . import cache, pool, rows, score, topk
 
 
 def decode_row_info(wl):
@@ -49,6 +49,21 @@ def decode_topk(wl, logits_by_row=None, requests=None):
     for r, lg in logits_by_row.items():
         out[r] = topk.topk_row(lg, int(L[r]), wl.topk)
     return out
+
+
+def decode_pool_topk(wl, pool_size, topk_pools, init_pools, local_pools, logits_by_row=None, requests=None):
+    """Pool-level selection of every grid row (or the requested requests'
+    rows; other rows stay -1): (tokens int32 [grid_rows, (topk_pools + 1)
+    * pool_size], pools int32 [grid_rows, topk_pools])."""
+    L, _ = decode_row_info(wl)
+    if logits_by_row is None:
+        logits_by_row = decode_logits(wl, requests)
+    R = wl.num_req * wl.next_n
+    toks = np.full((R, (topk_pools + 1) * pool_size), -1, dtype=np.int32)
+    pools = np.full((R, topk_pools), -1, dtype=np.int32)
+    for r, lg in logits_by_row.items():
+        toks[r], pools[r] = pool.pool_topk_row(lg, int(L[r]), pool_size, topk_pools, init_pools, local_pools)
+    return toks, pools
 
 
 def prefill_chunk_row_info(wl, rec):

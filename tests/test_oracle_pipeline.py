@@ -159,3 +159,19 @@ def test_prefill_chunk_rows_compressed(ratio):
     _, _, L, ks, _ = pipeline.prefill_chunk_row_info(wl, g["chunk"])
     assert L.tolist() == [x // ratio for x in g["rows"]["L"]]
     assert ks.tolist() == [0, 0, 5 // ratio]
+
+
+def test_decode_grid_pool_topk():
+    """The pool selection of the hand-worked grid, pools of 2 keys, one
+    place, no kept pools:
+      (0,0) L 3 [1.5, 1, 0.5]: one complete pool -> pool 0, tail key 2
+      (0,1) L 4 [0.5, -1, 0.5, 0.5]: maxima 0.5, 0.5 tie -> pool 0
+      (1,0) L 3: one complete pool -> pool 0, tail key 2
+      (1,1) padded -> nothing
+      (2,0) L 4 [1, 2, 4, 3]: maxima 2, 4 -> pool 1
+      (2,1) L 5 [1, -2, 0, 3, -1]: maxima 1, 3 -> pool 1, tail key 4"""
+    g, wl = _decode_wl()
+    toks, pools = pipeline.decode_pool_topk(wl, 2, 1, 0, 0)
+    assert pools[:, 0].tolist() == [0, 0, 0, -1, 1, 1]
+    assert toks.tolist() == [[0, 1, 2, -1], [0, 1, -1, -1], [0, 1, 2, -1], [-1, -1, -1, -1],
+                             [2, 3, -1, -1], [2, 3, 4, -1]]
