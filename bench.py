@@ -66,7 +66,9 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 CALIB_SUBSTR = "MulFunctor<float>"
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_decode_amd", "csrc")
-ALL_CONFIGS = ("C1", "C2", "C3", "C4", "C5")
+ALL_CONFIGS = ("C1", "C2", "C3", "C4", "C5", "P2")
+# pool-level workloads: (decode batch, pool size, pools kept, first kept, last kept)
+POOL_WORKLOADS = {"P2": ("C2", 64, 32, 1, 2)}
 WORKLOADS = {
     "C1": "tiny fp8 decode: 1 request, L=300, page 64, 8-page pool (random permutation), H=4, head_dim 32, "
           "top-k 64, next_n=1",
@@ -80,10 +82,12 @@ WORKLOADS = {
           "e4m3 keys + fp32 scales, page 64; planner chunks of <= 65536 keys and <= 512 MiB of logits (16 chunks)",
     "V4": "compressed fp8 decode: 64 requests x 131072 tokens, compress ratio 4 (32768 keys each), 256-token "
           "pages, H=64, head_dim 128, top-k 2048, fp8 e4m3 keys + fp32 scales",
+    "P2": "pool-level decode: the fp8 decode batch (32 requests, seq_len ~ U[4096, 32768], H=64, head_dim 128), "
+          "pools of 64 keys, 32 pools kept per row of which the first and the last two always",
 }
 # default rotated pool copies: enough that a pool is out of the MALL when it is read again
-DEFAULT_COPIES = {"C1": 1, "C2": 8, "C3": 2, "C4": 2, "V4": 2}
-CPU_BUDGET_S = {"C1": 2.0, "C2": 5.0, "C3": 6.0, "C4": 6.0, "C5": 8.0, "V4": 5.0}
+DEFAULT_COPIES = {"C1": 1, "C2": 8, "C3": 2, "C4": 2, "V4": 2, "P2": 8}
+CPU_BUDGET_S = {"C1": 2.0, "C2": 5.0, "C3": 6.0, "C4": 6.0, "C5": 8.0, "V4": 5.0, "P2": 4.0}
 PREFILL_WORKSPACE_TOKENS = 65536
 PREFILL_LOGITS_BYTES = 512 << 20
 
@@ -140,10 +144,14 @@ def decode_bytes(wl) -> dict:
     return b
 
 
-def scored_keys_decode(wl) -> int:
+def scored_keys_decode(wl, pools=None) -> int:
     """Keys the decode step scores: sum of L over rows with L > k (shorter
-    rows are causal-filled without scoring)."""
+    rows are causal-filled without scoring); for a pool selection, over rows
+    with more complete pools than pools kept."""
     L, _ = decode_rows(wl)
+    if pools is not None:
+        B, k = pools[0], pools[1]
+        return int(L[L // B > k].sum())
     return int(L[L > wl.topk].sum())
 
 
@@ -191,17 +199,22 @@ def oracle_threads() -> int:
         return 1
 
 
-def cpu_baseline_decode(wl, budget_s: float) -> dict:
+def cpu_baseline_decode(wl, budget_s: float, pools=None) -> dict:
     """The oracle on whole requests of the batch in order (cycling) for about
-    `budget_s` seconds: dequantise, fp64 logits, top-k."""
+    `budget_s` seconds: dequantise, fp64 logits, top-k (or the pool
+    selection)."""
     import oracle
     keys = rows = done = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b = done % wl.num_req
         lg = oracle.pipeline.decode_logits(wl, requests=[b])
-        oracle.pipeline.decode_topk(wl, lg, requests=[b])
-        keys += int(sum(len(v) for v in lg.values() if len(v) > wl.topk))
+        if pools is None:
+            oracle.pipeline.decode_topk(wl, lg, requests=[b])
+            keys += int(sum(len(v) for v in lg.values() if len(v) > wl.topk))
+        else:
+            oracle.pipeline.decode_pool_topk(wl, *pools, logits_by_row=lg, requests=[b])
+            keys += int(sum(len(v) for v in lg.values() if len(v) // pools[0] > pools[1]))
         rows += int(sum(1 for v in lg.values() if len(v)))
         done += 1
     dt = time.perf_counter() - t0
@@ -248,7 +261,8 @@ def cpu_baseline_prefill(wl, plan, budget_s: float) -> dict:
 def profile_name(cfg: str) -> str:
     return {"C1": "score_kernel_fp8_decode_tiny_c1", "C2": "score_kernel_fp8_decode_32req",
             "C3": "score_kernel_fp8_decode_mtp_c3", "C4": "score_kernel_mxfp4_decode_c4",
-            "C5": "score_block_kernel_fp8_prefill", "V4": "score_kernel_fp8_decode_compressed_v4"}[cfg]
+            "C5": "score_block_kernel_fp8_prefill", "V4": "score_kernel_fp8_decode_compressed_v4",
+            "P2": "score_kernel_fp8_decode_pool_p2"}[cfg]
 
 
 def load_traffic(cfg: str):
@@ -308,7 +322,7 @@ def capture(fn, n_inner: int):
 # Decode and prefill runs
 # ---------------------------------------------------------------------------
 
-def run_decode(wl, args) -> dict:
+def run_decode(wl, args, pools=None) -> dict:
     import numpy as np
     import torch
 
@@ -328,14 +342,29 @@ def run_decode(wl, args) -> dict:
     q = torch.from_numpy(wl.q.view(np.int16)).to(dev).view(torch.bfloat16)
     w = torch.from_numpy(wl.w).to(dev)
     k, R = wl.topk, rows.num_rows
-    outs = torch.empty((R, k), dtype=torch.int32, device=dev)
-    ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, caches[0], rows, wl.heads, k), dev)
+    if pools is not None:
+        pl = idx.pools(*pools)
+        outs = torch.empty((R, (pools[1] + 1) * pools[0]), dtype=torch.int32, device=dev)
+        ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_POOL_TOPK, caches[0], rows, wl.heads, 0),
+                               dev)
+    else:
+        outs = torch.empty((R, k), dtype=torch.int32, device=dev)
+        ws = idx.new_workspace(idx.idx_workspace_bytes(idx.IDX_OP_DECODE_TOPK, caches[0], rows, wl.heads, k), dev)
     ML = int(wl.seq_lens.max()) // wl.compress_ratio
     logits = torch.empty((R, max(-(-ML // 64) * 64, 64)), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
-        idx.idx_decode_topk(caches[i % copies], rows, q, w, k, outs, ws)
+        if pools is not None:
+            idx.idx_decode_pool_topk(caches[i % copies], rows, q, w, pl, outs, None, ws)
+        else:
+            idx.idx_decode_topk(caches[i % copies], rows, q, w, k, outs, ws)
+
+    def select(out):
+        if pools is not None:
+            idx.idx_pool_topk(logits, rows, pl, out, None, ws)
+        else:
+            idx.idx_topk(logits, rows, k, out, ws)
 
     if args.calib:
         src = torch.ones((args.calib_mib << 20) // 4, dtype=torch.float32, device=dev)
@@ -352,9 +381,9 @@ def run_decode(wl, args) -> dict:
     # the two launches called one by one give the same rows
     sep = torch.full_like(outs, -7)
     idx.idx_logits_paged(caches[0], rows, q, w, logits, ws)
-    idx.idx_topk(logits, rows, k, sep, ws)
+    select(sep)
     torch.cuda.synchronize()
-    assert torch.equal(first, sep), f"{wl.name}: idx_decode_topk differs from idx_logits_paged + idx_topk"
+    assert torch.equal(first, sep), f"{wl.name}: the one-call decode differs from the scorer + selection calls"
 
     # timed region: K whole steps back to back, wall clock between syncs
     step_ms = wall_ms(lambda i: step(args.warmup + i), args.steps)
@@ -373,13 +402,16 @@ def run_decode(wl, args) -> dict:
     # on the launch stream (the scorer on the rotated pools)
     score_ms = event_ms(stream, lambda i: idx.idx_logits_paged(caches[i % copies], rows, q, w, logits, ws),
                         args.steps)
-    topk_ms = event_ms(stream, lambda i: idx.idx_topk(logits, rows, k, sep, ws), args.steps)
+    topk_ms = event_ms(stream, lambda i: select(sep), args.steps)
     torch.cuda.synchronize()
     assert idx.idx_read_device_status(ws) == 0
 
-    keys = scored_keys_decode(wl)
+    keys = scored_keys_decode(wl, pools)
     _, real = decode_rows(wl)
     ab = decode_bytes(wl)
+    if pools is not None:   # the output is the expanded positions
+        ab["topk_out"] = R * (pools[1] + 1) * pools[0] * 4
+        ab["step"] = ab["scorer"] + ab["topk_out"]
     achieved = ab["scorer"] / (score_ms * 1e-3) / 1e9
     step_gbs = ab["step"] / (step_ms * 1e-3) / 1e9
     graph_gbs = ab["step"] / (graph_ms * 1e-3) / 1e9
@@ -501,17 +533,23 @@ def run_all(args):
     per = {}
     for name in names:
         print(f"[bench] {name}: generating", file=sys.stderr, flush=True)
-        wl = config(name)
+        pools = None
+        if name in POOL_WORKLOADS:
+            base, *pools = POOL_WORKLOADS[name]
+            wl = config(base)
+            wl.name = name
+        else:
+            wl = config(name)
         print(f"[bench] {name}: timing", file=sys.stderr, flush=True)
         if wl.kind == "prefill":
             res, plan = run_prefill(wl, args)
         else:
-            res, plan = run_decode(wl, args), None
+            res, plan = run_decode(wl, args, pools), None
         if not args.no_cpu_baseline:
             print(f"[bench] {name}: cpu baseline", file=sys.stderr, flush=True)
             budget = CPU_BUDGET_S.get(name, 5.0) * args.cpu_scale
             res["cpu_baseline"] = (cpu_baseline_prefill(wl, plan, budget) if plan is not None
-                                   else cpu_baseline_decode(wl, budget))
+                                   else cpu_baseline_decode(wl, budget, pools))
         res["workload"] = WORKLOADS[name]
         per[name] = res
         print(f"[bench] {name}: {res['value']:.4g} keys/s, step {res['ms_per_step']:.4f} ms, "
@@ -519,7 +557,7 @@ def run_all(args):
               file=sys.stderr, flush=True)
         del wl
     # headline: the largest workload measured (C5 by work, then C4, ...)
-    order = ["C5", "C4", "C3", "V4", "C2", "C1"]
+    order = ["C5", "C4", "C3", "V4", "C2", "P2", "C1"]
     head = next(n for n in order if n in per)
     h = per[head]
     line = {
@@ -616,7 +654,7 @@ def summarize(name, cfg, stats_dir, fetch_dir, write_dir, commands, bench_json=N
 
     from workloads import config
 
-    wl = config(cfg)
+    wl = config(POOL_WORKLOADS[cfg][0]) if cfg in POOL_WORKLOADS else config(cfg)
     kname = scorer_kernel_name(wl)
     out = {"workload": cfg, "kernel": kname, "source_hash": kernel_source_hash(), "commands": commands}
     stats = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)

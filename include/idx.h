@@ -158,6 +158,28 @@ int64_t idx_num_rows(const idx_rows* rows);
 #define IDX_OP_TOPK 1
 #define IDX_OP_DECODE_TOPK 2
 #define IDX_OP_CACHE_WRITE 3
+#define IDX_OP_POOL_TOPK 4         /* k is ignored */
+#define IDX_OP_DECODE_POOL_TOPK 5  /* k is ignored */
+
+/*
+ * Pool-level selection (the pool_topk / expand_pools_and_append_tail variant
+ * of the glm5next sparse_indexer page; the topk_blocks, init_blocks and
+ * local_blocks of the MiniMax-M3 mono runner page's indexer).  The pages do
+ * not define how a pool is scored; this library's reading: pool p of a row
+ * is the pool_size keys [p * pool_size, (p + 1) * pool_size); a row of L keys
+ * has n = L / pool_size complete pools and a tail of the last L % pool_size
+ * keys; a pool's score is the largest logit of its keys; the first
+ * init_pools and the last local_pools complete pools are always kept and
+ * count toward topk_pools; the other places go to the highest-scoring
+ * complete pools, ties to the lower pool index (-0.0 equal to +0.0); every
+ * complete pool is kept when n <= topk_pools.
+ */
+typedef struct idx_pools {
+  int32_t pool_size;    /* keys per pool: 16, 32, 64 or 128 */
+  int32_t topk_pools;   /* pools kept per row, 1..512 */
+  int32_t init_pools;   /* >= 0 */
+  int32_t local_pools;  /* >= 0, init_pools + local_pools <= topk_pools */
+} idx_pools;
 
 /*
  * Bytes of device workspace `op` needs for these arguments.  The caller
@@ -229,6 +251,35 @@ idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* 
 idx_status idx_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q,
                            const float* w, int32_t heads, int32_t k, int32_t* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Pool-level top-k of rows of logits (same rows and logits layout as
+ * idx_topk).  Per row:
+ *   out_tokens[r * W .. r * W + W), W = (topk_pools + 1) * pool_size: the
+ *       kept pools' key positions in ascending order, then the tail keys
+ *       n * pool_size .. L - 1 (appended whatever their logits), -1 padded;
+ *       padded rows (L = 0) are all -1;
+ *   out_pools[r * topk_pools ..] (optional, may be NULL): the kept pool
+ *       indices, ascending, -1 padded.
+ * Rows may hold at most 8192 complete pools (max_seq_len / compress_ratio /
+ * pool_size <= 8192, checked on the host).  Workspace:
+ * idx_workspace_bytes(IDX_OP_POOL_TOPK, NULL, rows, 0, 0) (the status word).
+ */
+idx_status idx_pool_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, const idx_pools* pools,
+                         int32_t* out_tokens, int32_t* out_pools, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Decode scoring followed by the pool-level selection of every DECODE row
+ * (the decode path of the glm5next page's pool indexer: logits on the padded
+ * grid, then pool_topk and the expansion): the scorer writes each row's
+ * logits into the workspace, the pool selection reads them.  Output as
+ * idx_pool_topk.  Workspace: idx_workspace_bytes(IDX_OP_DECODE_POOL_TOPK,
+ * cache, rows, heads, 0) (the status word and the row logits).
+ */
+idx_status idx_decode_pool_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q, const float* w,
+                                int32_t heads, const idx_pools* pools, int32_t* out_tokens, int32_t* out_pools,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * idx_decode_topk for callers that cannot allocate device memory (code under

@@ -14,11 +14,17 @@ from .binding import (  # noqa: F401
     IDX_OP_DECODE_TOPK,
     IDX_OP_LOGITS,
     IDX_OP_TOPK,
+    IDX_OP_POOL_TOPK,
+    IDX_OP_DECODE_POOL_TOPK,
+    IdxPools,
     IDX_DEV_BAD_PAGE,
     IDX_DEV_BAD_SLOT,
     idx_cache_write,
     idx_decode_topk,
     idx_decode_topk_noalloc,
+    idx_decode_pool_topk,
+    idx_pool_topk,
+    pools,
     idx_logits_paged,
     idx_prefill_chunks,
     idx_read_device_status,

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libidx.so")
 
 SOURCES = ["idx_lib.hip", "planner.cpp"]
-HEADERS = ["device_common.cuh", "idx_internal.h", "score.cuh", "select.cuh", "topk.cuh"]
+HEADERS = ["cache_write.cuh", "device_common.cuh", "idx_internal.h", "pool.cuh", "score.cuh", "select.cuh",
+           "topk.cuh"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -21,6 +21,7 @@ IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_ENOSPC, IDX_EHIP = 0, 1, 2, 3, 4
 IDX_FMT_FP8_E4M3, IDX_FMT_MXFP4 = 0, 1
 IDX_ROWS_DECODE, IDX_ROWS_PREFILL = 0, 1
 IDX_OP_LOGITS, IDX_OP_TOPK, IDX_OP_DECODE_TOPK, IDX_OP_CACHE_WRITE = 0, 1, 2, 3
+IDX_OP_POOL_TOPK, IDX_OP_DECODE_POOL_TOPK = 4, 5
 IDX_DEV_BAD_PAGE, IDX_DEV_BAD_SLOT = 1, 2
 
 FMT_CODES = {"fp8": IDX_FMT_FP8_E4M3, "mxfp4": IDX_FMT_MXFP4}
@@ -32,6 +33,8 @@ EXPORTED = (
     "idx_topk",
     "idx_decode_topk",
     "idx_decode_topk_noalloc",
+    "idx_pool_topk",
+    "idx_decode_pool_topk",
     "idx_cache_write",
     "idx_prefill_chunks",
     "idx_read_device_status",
@@ -59,6 +62,11 @@ class IdxChunk(ctypes.Structure):
     _fields_ = [("req_begin", c_int32), ("req_end", c_int32), ("q_begin", c_int32),
                 ("q_end", c_int32), ("total_seq_lens", c_int64), ("token_begin", c_int64),
                 ("token_end", c_int64), ("skip_kv_gather", c_int32), ("over_budget", c_int32)]
+
+
+class IdxPools(ctypes.Structure):
+    _fields_ = [("pool_size", c_int32), ("topk_pools", c_int32), ("init_pools", c_int32),
+                ("local_pools", c_int32)]
 
 
 class IdxError(RuntimeError):
@@ -97,6 +105,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.idx_decode_topk_noalloc.argtypes = [POINTER(IdxCache), POINTER(IdxRows), c_void_p, c_void_p, c_int32,
                                             c_int32, c_void_p, c_void_p, c_void_p]
     lib.idx_decode_topk_noalloc.restype = c_int32
+    lib.idx_pool_topk.argtypes = [c_void_p, c_int64, POINTER(IdxRows), POINTER(IdxPools), c_void_p, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]
+    lib.idx_pool_topk.restype = c_int32
+    lib.idx_decode_pool_topk.argtypes = [POINTER(IdxCache), POINTER(IdxRows), c_void_p, c_void_p, c_int32,
+                                         POINTER(IdxPools), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.idx_decode_pool_topk.restype = c_int32
     lib.idx_cache_write.argtypes = [POINTER(IdxCache), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t,
                                     c_void_p]
     lib.idx_cache_write.restype = c_int32
@@ -237,6 +251,34 @@ def idx_decode_topk_noalloc(cache: Cache, rows: Rows, q: torch.Tensor, w: torch.
     _check("idx_decode_topk_noalloc", load().idx_decode_topk_noalloc(
         ctypes.byref(cache.c), ctypes.byref(rows.c), q.data_ptr(), w.data_ptr(), q.shape[1], k,
         out.data_ptr(), _ptr(status), _stream(stream)))
+
+
+def pools(pool_size: int, topk_pools: int, init_pools: int = 0, local_pools: int = 0) -> IdxPools:
+    """Pool-selection parameters (idx_pools)."""
+    return IdxPools(pool_size, topk_pools, init_pools, local_pools)
+
+
+def idx_pool_topk(logits: torch.Tensor, rows: Rows, pl: IdxPools, out_tokens: torch.Tensor,
+                  out_pools: torch.Tensor | None, workspace: torch.Tensor, stream=None) -> None:
+    """out_tokens: int32 [rows, (topk_pools + 1) * pool_size]; out_pools:
+    int32 [rows, topk_pools] or None."""
+    assert logits.dtype == torch.float32 and logits.stride(-1) == 1
+    assert out_tokens.dtype == torch.int32 and out_tokens.is_contiguous()
+    assert out_pools is None or (out_pools.dtype == torch.int32 and out_pools.is_contiguous())
+    _check("idx_pool_topk", load().idx_pool_topk(
+        logits.data_ptr(), _row_stride(logits), ctypes.byref(rows.c), ctypes.byref(pl), out_tokens.data_ptr(),
+        _ptr(out_pools), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def idx_decode_pool_topk(cache: Cache, rows: Rows, q: torch.Tensor, w: torch.Tensor, pl: IdxPools,
+                         out_tokens: torch.Tensor, out_pools: torch.Tensor | None, workspace: torch.Tensor,
+                         stream=None) -> None:
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and w.dtype == torch.float32 and w.is_contiguous()
+    assert out_tokens.dtype == torch.int32 and out_tokens.is_contiguous()
+    assert out_pools is None or (out_pools.dtype == torch.int32 and out_pools.is_contiguous())
+    _check("idx_decode_pool_topk", load().idx_decode_pool_topk(
+        ctypes.byref(cache.c), ctypes.byref(rows.c), q.data_ptr(), w.data_ptr(), q.shape[1], ctypes.byref(pl),
+        out_tokens.data_ptr(), _ptr(out_pools), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def idx_cache_write(cache: Cache, k: torch.Tensor, slot_mapping: torch.Tensor, workspace: torch.Tensor,

@@ -9,6 +9,7 @@
 #include "../../include/idx.h"
 #include "idx_internal.h"
 #include "cache_write.cuh"
+#include "pool.cuh"
 #include "score.cuh"
 #include "topk.cuh"
 
@@ -278,6 +279,37 @@ idx_status check_ws(void* ws, size_t have, size_t need) {
   return IDX_OK;
 }
 
+// Pool selection arguments, against the rows' longest row.
+idx_status check_pools(const idx_pools* pl, const RowArgs& R, int& lg) {
+  if (!pl) return fail(IDX_EINVAL, "pools descriptor is null");
+  lg = pl->pool_size == 16 ? 4 : pl->pool_size == 32 ? 5 : pl->pool_size == 64 ? 6 : pl->pool_size == 128 ? 7 : -1;
+  if (lg < 0) return fail(IDX_EUNSUPPORTED, "pool_size must be 16, 32, 64 or 128");
+  if (pl->topk_pools < 1) return fail(IDX_EINVAL, "topk_pools must be >= 1");
+  if (pl->topk_pools > kMaxPoolTopk) return fail(IDX_EUNSUPPORTED, "topk_pools must be <= 512");
+  if (pl->init_pools < 0 || pl->local_pools < 0 ||
+      static_cast<int64_t>(pl->init_pools) + pl->local_pools > pl->topk_pools)
+    return fail(IDX_EINVAL, "init_pools and local_pools must be >= 0 with a sum <= topk_pools");
+  if ((static_cast<int64_t>(R.max_keys) >> lg) > kMaxPools)
+    return fail(IDX_EUNSUPPORTED, "rows of more than 8192 complete pools");
+  return IDX_OK;
+}
+
+idx_status launch_pool_topk(const float* logits, int64_t stride, const RowArgs& R, const idx_pools* pl, int lg,
+                            int32_t* out_tokens, int32_t* out_pools, hipStream_t s) {
+  PoolParams p{};
+  p.logits = logits;
+  p.stride = stride;
+  p.rows = R;
+  p.pool_log2 = lg;
+  p.topk = pl->topk_pools;
+  p.init_pools = pl->init_pools;
+  p.local_pools = pl->local_pools;
+  p.out_tokens = out_tokens;
+  p.out_pools = out_pools;
+  hipLaunchKernelGGL(pool_topk_kernel<kPoolThreads>, dim3(R.num_rows), dim3(kPoolThreads), 0, s, p);
+  return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
+}
+
 // Argument checks shared by the two decode top-k entry points.
 idx_status check_decode_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q, const float* w,
                              int heads, int k, const int32_t* out, CacheArgs& C, RowArgs& R) {
@@ -294,26 +326,32 @@ idx_status check_decode_topk(const idx_cache* cache, const idx_rows* rows, const
   return IDX_OK;
 }
 
+// Decode scorer into row logits scratch_stride(R) apart.
+idx_status launch_decode_scorer(const CacheArgs& C, const RowArgs& R, const uint16_t* q, const float* w,
+                                int heads, float* logits, int32_t* header, hipStream_t s) {
+  const int rg = pick_rg(R);
+  ScoreParams p{};
+  p.cache = C;
+  p.rows = R;
+  p.q = q;
+  p.w = w;
+  p.heads = heads;
+  p.logits = logits;
+  p.logits_stride = scratch_stride(R);
+  p.header = header;
+  p.num_groups = static_cast<int32_t>(group_bound(R, rg));
+  if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
+  return IDX_OK;
+}
+
 // Scorer into the scratch's row logits (after its 256-byte header), then
 // top-k of each row (the kernel boundary orders the two); long rows' chunk
 // candidates follow the row logits.
 idx_status run_decode_topk(const CacheArgs& C, const RowArgs& R, const uint16_t* q, const float* w, int heads,
                            int k, int32_t* out, uint8_t* ws, int32_t* header, hipStream_t s) {
   float* logits = reinterpret_cast<float*>(ws + scratch_offset());
-  if (R.max_keys > 0) {
-    const int rg = pick_rg(R);
-    ScoreParams p{};
-    p.cache = C;
-    p.rows = R;
-    p.q = q;
-    p.w = w;
-    p.heads = heads;
-    p.logits = logits;
-    p.logits_stride = scratch_stride(R);
-    p.header = header;
-    p.num_groups = static_cast<int32_t>(group_bound(R, rg));
-    if (dispatch_score(p, score_grid(R, rg), s) != hipSuccess) return fail(IDX_EHIP, "kernel launch failed");
-  }
+  idx_status st = IDX_OK;
+  if (R.max_keys > 0 && (st = launch_decode_scorer(C, R, q, w, heads, logits, header, s)) != IDX_OK) return st;
   return launch_topk(logits, scratch_stride(R), R, k, out, ws + decode_ws_bytes(R), s);
 }
 
@@ -358,6 +396,7 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
     if (k < 1 || k > kMaxK) return 0;
     return kStatusBytes + topk_chunk_bytes(R, k);
   }
+  if (op == IDX_OP_POOL_TOPK) return check_rows(rows, false, R) == IDX_OK ? kStatusBytes : 0;
   CacheArgs C;
   if (check_cache(cache, C) != IDX_OK || check_rows(rows, true, R) != IDX_OK) return 0;
   if (heads < 1 || heads > kMaxHeads) return 0;
@@ -366,6 +405,7 @@ size_t idx_workspace_bytes(int32_t op, const idx_cache* cache, const idx_rows* r
     if (R.kind != IDX_ROWS_DECODE || k < 1 || k > kMaxK) return 0;
     return decode_ws_bytes(R) + topk_chunk_bytes(R, k);
   }
+  if (op == IDX_OP_DECODE_POOL_TOPK) return R.kind == IDX_ROWS_DECODE ? decode_ws_bytes(R) : 0;
   return 0;
 }
 
@@ -480,6 +520,41 @@ idx_status idx_decode_topk_noalloc(const idx_cache* cache, const idx_rows* rows,
   // there is none (nobody reads that one, so it needs no clearing)
   int32_t* header = status ? reinterpret_cast<int32_t*>(status) : reinterpret_cast<int32_t*>(ws);
   return run_decode_topk(C, R, q, w, heads, k, out, ws, header, static_cast<hipStream_t>(stream));
+}
+
+idx_status idx_pool_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, const idx_pools* pools,
+                         int32_t* out_tokens, int32_t* out_pools, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  RowArgs R;
+  idx_status st = check_rows(rows, false, R);
+  if (st != IDX_OK) return st;
+  if (!logits || !out_tokens || logits_stride < 0) return fail(IDX_EINVAL, "logits or out_tokens is null, or logits_stride < 0");
+  int lg = 0;
+  if ((st = check_pools(pools, R, lg)) != IDX_OK) return st;
+  if (R.kind == IDX_ROWS_DECODE && logits_stride < R.max_keys) return fail(IDX_EINVAL, "logits_stride < max_seq_len / compress_ratio");
+  if ((st = check_ws(workspace, workspace_bytes, kStatusBytes)) != IDX_OK) return st;
+  if (R.num_rows == 0) return IDX_OK;
+  return launch_pool_topk(logits, logits_stride, R, pools, lg, out_tokens, out_pools, static_cast<hipStream_t>(stream));
+}
+
+idx_status idx_decode_pool_topk(const idx_cache* cache, const idx_rows* rows, const uint16_t* q, const float* w,
+                                int32_t heads, const idx_pools* pools, int32_t* out_tokens, int32_t* out_pools,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  CacheArgs C;
+  RowArgs R;
+  // the token top-k's checks with a placeholder k (the pools replace it)
+  idx_status st = check_decode_topk(cache, rows, q, w, heads, 1, out_tokens, C, R);
+  if (st != IDX_OK) return st;
+  int lg = 0;
+  if ((st = check_pools(pools, R, lg)) != IDX_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, decode_ws_bytes(R))) != IDX_OK) return st;
+  if (R.num_rows == 0) return IDX_OK;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + scratch_offset());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (R.max_keys > 0 && (st = launch_decode_scorer(C, R, q, w, heads, logits, reinterpret_cast<int32_t*>(ws), s)) != IDX_OK)
+    return st;
+  return launch_pool_topk(logits, scratch_stride(R), R, pools, lg, out_tokens, out_pools, s);
 }
 
 idx_status idx_read_device_status(void* workspace, uint32_t* flags, void* stream) {

@@ -19,11 +19,11 @@ struct TopkParams {
 };
 
 // Key count L and logits column base of row r (DECODE grid row or PREFILL
-// chunk row); every thread of the workgroup gets the same values.
+// chunk row); every thread of the workgroup gets the same values.  `scan`
+// holds NT / 64 ints of LDS.
 template <int NT>
-__device__ __forceinline__ void row_window(const TopkParams& p, int r, int& L_out, int& col0_out,
-                                           SelectShared<NT>& sm, int (&info)[2]) {
-  const RowArgs& R = p.rows;
+__device__ __forceinline__ void row_window(const RowArgs& R, int r, int& L_out, int& col0_out, int* scan,
+                                           int (&info)[2]) {
   int L = 0, col0 = 0;
   if (R.kind == 0) {
     const int b = r / R.next_n;
@@ -50,7 +50,7 @@ __device__ __forceinline__ void row_window(const TopkParams& p, int r, int& L_ou
     for (int j = threadIdx.x; j < b; j += NT) {
       part += request_keys(R.seq_lens[j], R.max_len, R.ratio);
     }
-    col0 = block_sum_int(part, sm.scan, NT);
+    col0 = block_sum_int(part, scan, NT);
     int seq = R.seq_lens[b];
     seq = seq > R.max_len ? R.max_len : seq;
     const int qlen = R.qsl[b + 1] - R.qsl[b];
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   __shared__ int info[2];
   const int r = blockIdx.x;
   int L, col0;
-  row_window<NT>(p, r, L, col0, sm, info);
+  row_window<NT>(p.rows, r, L, col0, sm.scan, info);
   select_row<NT, kReg>(p.logits + static_cast<int64_t>(r) * p.stride + col0, L, p.k,
                        p.out + static_cast<int64_t>(r) * p.k, sm);
 }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   const int c = blockIdx.x / nr;
   const int r = blockIdx.x - c * nr;
   int L, col0;
-  row_window<NT>(p, r, L, col0, sm, info);
+  row_window<NT>(p.rows, r, L, col0, sm.scan, info);
   const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
   if (L <= kRowCap) {
     if (c == 0) select_row<NT>(row, L, p.k, p.out + static_cast<int64_t>(r) * p.k, sm);
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   __shared__ int info[2];
   const int r = blockIdx.x;
   int L, col0;
-  row_window<NT>(p, r, L, col0, sm, info);
+  row_window<NT>(p.rows, r, L, col0, sm.scan, info);
   if (L <= kRowCap) return;  // finished by its chunk
   const int k = p.k;
   const int nc = (L + kRowCap - 1) / kRowCap;

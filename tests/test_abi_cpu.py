@@ -250,3 +250,36 @@ def test_noalloc_host_checks(lib):
     empty = _rows(num_req=0)
     assert lib.idx_decode_topk_noalloc(ctypes.byref(c), ctypes.byref(empty), FAKE, FAKE, 64, 16, FAKE, None,
                                        None) == B.IDX_OK
+
+
+def test_pool_host_checks(lib):
+    """Pool selection: parameter checks on the host, workspace sizes."""
+    E, U, S = B.IDX_EINVAL, B.IDX_EUNSUPPORTED, B.IDX_ENOSPC
+    r = _rows(max_seq_len=300)
+
+    def pt(pools, rows=r, out=FAKE, ws=FAKE, wsb=256, stride=512):
+        return lib.idx_pool_topk(FAKE, stride, ctypes.byref(rows), ctypes.byref(pools) if pools else None, out,
+                                 None, ws, wsb, None)
+
+    assert pt(None) == E
+    assert pt(B.IdxPools(48, 8, 0, 0)) == U                   # pool size
+    assert pt(B.IdxPools(64, 0, 0, 0)) == E                   # no place
+    assert pt(B.IdxPools(64, 513, 0, 0)) == U
+    assert pt(B.IdxPools(64, 8, 5, 4)) == E                   # kept by position > topk
+    assert pt(B.IdxPools(64, 8, -1, 0)) == E
+    assert pt(B.IdxPools(64, 8, 1, 1), out=None) == E
+    assert pt(B.IdxPools(64, 8, 1, 1), stride=100) == E       # stride < max_seq_len
+    assert pt(B.IdxPools(64, 8, 1, 1), wsb=16) == S
+    long_rows = _rows(max_seq_len=131072 + 16, bt_width=2049, bt_stride=2049)
+    assert pt(B.IdxPools(16, 8, 1, 1), rows=long_rows, stride=1 << 20) == U   # 8193 pools
+    assert pt(B.IdxPools(64, 8, 1, 1), rows=_rows(num_req=0)) == B.IDX_OK
+    c = _cache()
+    assert lib.idx_workspace_bytes(B.IDX_OP_POOL_TOPK, None, ctypes.byref(r), 0, 0) == 256
+    assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_POOL_TOPK, ctypes.byref(c), ctypes.byref(r), 64, 0) == \
+        lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 64, 16)
+    need = lib.idx_workspace_bytes(B.IDX_OP_DECODE_POOL_TOPK, ctypes.byref(c), ctypes.byref(r), 64, 0)
+    pl = B.IdxPools(64, 8, 1, 1)
+    assert lib.idx_decode_pool_topk(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, 64, ctypes.byref(pl), FAKE, None,
+                                    FAKE, need - 1, None) == S
+    assert lib.idx_decode_pool_topk(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, 64, None, FAKE, None,
+                                    FAKE, need, None) == E
