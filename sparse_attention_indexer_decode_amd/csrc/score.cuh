@@ -845,8 +845,10 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
   decode_page_slice<D, MX>(sm.ring[0], sm.dec[0], wave);
 
   // Per page j: one barrier publishes raw page j + 1 and decoded page j and
-  // frees the buffers of page j - 1; then page j + kRing - 1 is requested,
-  // page j + 1 decoded, and page j scored.  Scoring is software-pipelined
+  // frees the buffers of page j - 1; then page j + kRing - 1 is requested
+  // and page j scored, with page j + 1 decoded between its two tiles (so the
+  // decode's LDS round trip runs under the first tile's MFMAs instead of
+  // stalling every wave right after the barrier).  Scoring is software-pipelined
   // over 32-key tiles: the MFMAs of a tile are issued next to the head sums
   // of the tile before it (independent work the SIMD overlaps), alternating
   // between two accumulator sets.  The range is walked one group at a time,
@@ -871,13 +873,14 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
         const int nxt = id_of(j + kRing - 1);
         dma_page<D, MX>(p, nxt, lds_addr(sm.ring[(i + kRing - 1) % kRing]));
       }
-      if (j + 1 < j1) decode_page_slice<D, MX>(sm.ring[(i + 1) % kRing], sm.dec[(i + 1) & 1], wave);
       const v8bf* dec = sm.dec[i & 1];
       const uint8_t* raw = sm.ring[i % kRing];
       const int base = (j - g_first) * kPage * 4 + key_off;
       tile_mfma<D, MX, MT>(dec, raw, 0, qf, acc0, ks0);
       tile_logits<MT>(acc1, ks1, wf, out, off1);
       __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
+      if (j + 1 < j1) decode_page_slice<D, MX>(sm.ring[(i + 1) % kRing], sm.dec[(i + 1) & 1], wave);
+      __builtin_amdgcn_sched_barrier(0);
       tile_mfma<D, MX, MT>(dec, raw, 1, qf, acc1, ks1);
       tile_logits<MT>(acc0, ks0, wf, out, base);
       __builtin_amdgcn_sched_barrier(0);
