@@ -54,8 +54,13 @@ constexpr int kBitmapWords = 4096;  // bitmap path for rows up to 131072 keys
 constexpr int kRankCap = 256;       // threshold-bin keys ranked pairwise
 constexpr int kRowCap = 32768;      // keys of an LDS-resident row
 
+// The 512-thread instantiation is the streaming-only kernel (no register
+// path): its second-digit histogram shares the union below with the first
+// digit's histogram and the bitmap, which are never live at the same time on
+// the streaming path, so that three of its workgroups fit a CU's LDS.
 template <int NT>
 struct SelectShared {
+  static constexpr bool kShareHist2 = NT == 512;
   struct {
     uint32_t ckey[kCandCap];
     int cidx[kCandCap];
@@ -63,10 +68,12 @@ struct SelectShared {
   union {
     int hist1[kD1Bins];          // first-digit histogram (when not given)
     uint32_t sel[kBitmapWords];  // winners, one bit per position
+    int hist2s[2048];            // second-digit histogram (streaming-only kernel)
   } u;
-  int hist2[2048];
+  int hist2o[kShareHist2 ? 1 : 2048];
   int scan[NT / kWave];
   int bc[8];
+  __device__ __forceinline__ int* hist2() { return kShareHist2 ? u.hist2s : hist2o; }
 };
 
 struct SelectState {
@@ -181,7 +188,7 @@ __device__ __forceinline__ void find_digit(int nbins, int need, BinFn bin, Selec
 
 // d1 histogram of a row into sm.u.hist1.
 template <int NT>
-__device__ void row_histogram(const float* __restrict__ row, int L, bool aligned, SelectShared<NT>& sm) {
+__device__ __forceinline__ void row_histogram(const float* __restrict__ row, int L, bool aligned, SelectShared<NT>& sm) {
   const int tid = threadIdx.x;
   for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
   __syncthreads();
@@ -204,23 +211,23 @@ __device__ void row_histogram(const float* __restrict__ row, int L, bool aligned
 // number of elements in the chosen digit (equal to the updated st.need when
 // that digit is taken whole).
 template <int NT, class ForEach>
-__device__ int refine_pass(SelectState& st, int shift, int bits, ForEach for_each, SelectShared<NT>& sm) {
+__device__ __forceinline__ int refine_pass(SelectState& st, int shift, int bits, ForEach for_each, SelectShared<NT>& sm) {
   const int tid = threadIdx.x;
   const int nb = 1 << bits;
   const uint32_t dmask = static_cast<uint32_t>(nb - 1);
-  for (int j = tid; j < nb; j += NT) sm.hist2[j] = 0;
+  for (int j = tid; j < nb; j += NT) sm.hist2()[j] = 0;
   __syncthreads();
   const uint32_t prefix = st.prefix, pmask = st.pmask;
   for_each([&](uint32_t key) {
-    if ((key & pmask) == prefix) atomicAdd(&sm.hist2[(key >> shift) & dmask], 1);
+    if ((key & pmask) == prefix) atomicAdd(&sm.hist2()[(key >> shift) & dmask], 1);
   });
   __syncthreads();
   int digit, above, cnt;
   if (nb >= NT) {
-    find_digit<NT>(nb, st.need, [&](int d) { return sm.hist2[d]; }, sm, digit, above, cnt);
+    find_digit<NT>(nb, st.need, [&](int d) { return sm.hist2()[d]; }, sm, digit, above, cnt);
   } else {
     // fewer bins than threads: pad the digit space to NT bins
-    find_digit<NT>(NT, st.need, [&](int d) { return d < nb ? sm.hist2[d] : 0; }, sm, digit, above, cnt);
+    find_digit<NT>(NT, st.need, [&](int d) { return d < nb ? sm.hist2()[d] : 0; }, sm, digit, above, cnt);
   }
   st.prefix |= static_cast<uint32_t>(digit) << shift;
   st.pmask |= dmask << shift;
@@ -230,7 +237,7 @@ __device__ int refine_pass(SelectState& st, int shift, int bits, ForEach for_eac
 
 // Two radix steps (the second skipped when the first digit is taken whole).
 template <int NT, class ForEach>
-__device__ int refine(SelectState& st, int shift0, int bits0, int shift1, int bits1, ForEach for_each,
+__device__ __forceinline__ int refine(SelectState& st, int shift0, int bits0, int shift1, int bits1, ForEach for_each,
                       SelectShared<NT>& sm) {
   int cnt = refine_pass<NT>(st, shift0, bits0, for_each, sm);
   if (st.need != cnt) cnt = refine_pass<NT>(st, shift1, bits1, for_each, sm);
@@ -239,7 +246,7 @@ __device__ int refine(SelectState& st, int shift0, int bits0, int shift1, int bi
 
 // Ordered compaction straight from the global row (fallback path).
 template <int NT>
-__device__ void compact_global(const float* __restrict__ row, int L, int k, bool aligned, const SelectState& st,
+__device__ __forceinline__ void compact_global(const float* __restrict__ row, int L, int k, bool aligned, const SelectState& st,
                                int* __restrict__ out, SelectShared<NT>& sm) {
   const int tid = threadIdx.x;
   int run_sel = 0, run_eq = 0;
@@ -281,12 +288,173 @@ __device__ void compact_global(const float* __restrict__ row, int L, int k, bool
   }
 }
 
+// Appends every key of the row at or above `lo_key` (with its position) to
+// the LDS candidate list, at most kCandCap of them; returns how many there
+// are (also when more than fit).  Per-thread counts, one wave scan and one
+// reservation per wave and chunk; order irrelevant.
+template <int NT>
+__device__ __forceinline__ int collect_candidates(const float* __restrict__ row, int L, bool aligned,
+                                                  uint32_t lo_key, SelectShared<NT>& sm) {
+  if (threadIdx.x == 0) sm.bc[4] = 0;
+  __syncthreads();
+  constexpr int V = 8;
+  const int lane = lane_id();
+  for (int base = 0; base < L; base += NT * 4 * V) {
+    uint32_t u[4 * V];
+    bool v[4 * V];
+    load_keys_strided<V, NT>(row, base, L, aligned, u, v);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4 * V; ++j) c += (v[j] && u[j] >= lo_key) ? 1 : 0;
+    const int incl = wave_inclusive_scan(c);
+    const int wave_total = __shfl(incl, kWave - 1, kWave);
+    int wbase = 0;
+    if (lane == kWave - 1 && wave_total > 0) wbase = atomicAdd(&sm.bc[4], wave_total);
+    wbase = __shfl(wbase, kWave - 1, kWave);
+    int pos = wbase + incl - c;
+#pragma unroll
+    for (int j = 0; j < 4 * V; ++j) {
+      if (v[j] && u[j] >= lo_key) {
+        if (pos < kCandCap) {
+          sm.c.ckey[pos] = u[j];
+          sm.c.cidx[pos] = strided_pos<NT>(base, j);
+        }
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  return sm.bc[4];
+}
+
+// Steps 4 and 5 of a streamed row whose `nc` candidates (every key of the
+// top k among them) are in LDS and whose threshold state `st` has been
+// refined to the digit holding the k-th largest (n_eq keys match it): the
+// winners go to a position bitmap (those equal to the threshold key, when
+// not all are taken, by lowest position), then one ordered scan writes the k
+// positions.  Needs L <= kBitmapWords * 32.
+template <int NT>
+__device__ __forceinline__ void finish_candidates(int L, int k, const SelectState& st, int n_eq, int nc,
+                                                  int* __restrict__ out, SelectShared<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int W = (L + 31) >> 5;
+  const bool take_all_eq = st.need == n_eq;
+  const uint32_t tprefix = st.prefix, tmask = st.pmask;
+  // keys equal to the threshold, when not all are taken: the `need` lowest
+  // positions among them, i.e. the largest of (2^17 - 1 - position), by radix
+  // select on 17 bits (before the bitmap: the second-digit histogram may
+  // share its memory)
+  SelectState ts{0u, 0u, st.need};
+  if (!take_all_eq) {
+    refine<NT>(ts, 8, 9, 0, 8, [&](auto fn) {
+      for (int i = tid; i < nc; i += NT)
+        if ((sm.c.ckey[i] & tmask) == tprefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.c.cidx[i]));
+    }, sm);
+  }
+  for (int j = tid; j < W; j += NT) sm.u.sel[j] = 0u;
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) {
+    const uint32_t m = sm.c.ckey[i] & tmask;
+    const int p = sm.c.cidx[i];
+    const bool win = m > tprefix ||
+                     (m == tprefix && (take_all_eq || (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix));
+    if (win) atomicOr(&sm.u.sel[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+
+  // ordered emission
+  const int wpt = (W + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  const int w1 = (w0 + wpt < W) ? w0 + wpt : W;
+  int c_sel = 0;
+  for (int wd = w0; wd < w1; ++wd) c_sel += __popc(sm.u.sel[wd]);
+  int tot;
+  int pos = block_exclusive_scan<NT>(c_sel, tot, sm.scan);
+  for (int wd = w0; wd < w1; ++wd) {
+    uint32_t sel = sm.u.sel[wd];
+    while (sel) {
+      const int bpos = __builtin_ctz(sel);
+      sel &= sel - 1u;
+      out[pos++] = wd * 32 + bpos;
+    }
+  }
+  __syncthreads();
+}
+
+// Rows this long (and of at most kBitmapWords * 32 keys) with k at most
+// kSampleMaxK first try one read (the candidate window [k, kCandCap] around
+// the expected 1.5 k keeps a fallback rare):
+constexpr int kSampleMinLen = 16384;
+constexpr int kSampleMaxK = 2048;
+
+// One-read selection of a streamed row: a systematic sample (every S-th
+// 64-key block, at most kCandCap keys) gives a key K0 that about 1.5 k of the
+// row's keys reach -- the sample's ceil(1.5 k / S)-th largest -- and one pass
+// collects every key >= K0.  When that holds at least k and at most
+// kCandCap keys, every key of the top k is among them (the top k are >= the
+// k-th largest >= K0, since at least k keys are >= K0) and the exact
+// selection runs on them; otherwise (a skewed sample, heavy ties) nothing is
+// written and the caller takes the two-read path.  Returns whether it
+// finished the row (the same on every thread).
+template <int NT>
+__device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row, int L, int k, bool aligned,
+                                                   int* __restrict__ out, SelectShared<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int nb = L >> 6;                                  // full 64-key blocks
+  const int S = (nb + 63) / 64 > 16 ? (nb + 63) / 64 : 16;   // stride: >= 16, and <= 64 sampled blocks
+  const int ns_blocks = (nb + S - 1) / S;
+  const int ns = ns_blocks * 64;                         // <= 64 * 64 = kCandCap keys
+  static_assert(64 * 64 <= kCandCap, "the sample must fit the candidate area");
+  const int r = (3 * k + 2 * S - 1) / (2 * S);            // ceil(1.5 k / S)
+  if (r < 1 || r > ns) return false;
+  for (int qi = tid; qi < ns_blocks * 16; qi += NT) {
+    const int pos = (qi >> 4) * S * 64 + (qi & 15) * 4;
+    float f0, f1, f2, f3;
+    if (aligned) {
+      const float4 x = *reinterpret_cast<const float4*>(row + pos);
+      f0 = x.x; f1 = x.y; f2 = x.z; f3 = x.w;
+    } else {
+      f0 = row[pos]; f1 = row[pos + 1]; f2 = row[pos + 2]; f3 = row[pos + 3];
+    }
+    sm.c.ckey[4 * qi] = ordered_key(f0);
+    sm.c.ckey[4 * qi + 1] = ordered_key(f1);
+    sm.c.ckey[4 * qi + 2] = ordered_key(f2);
+    sm.c.ckey[4 * qi + 3] = ordered_key(f3);
+  }
+  __syncthreads();
+  // the lower edge of the 22-bit digit bin holding the sample's r-th largest
+  // key (or of its 11-bit bin when that is taken whole): only lower, never
+  // higher, than the r-th largest
+  SelectState ss{0u, 0u, r};
+  auto in_sample = [&](auto fn) {
+    for (int i = tid; i < ns; i += NT) fn(sm.c.ckey[i]);
+  };
+  const int cnt = refine_pass<NT>(ss, 21, 11, in_sample, sm);
+  if (ss.need != cnt) refine_pass<NT>(ss, 10, 11, in_sample, sm);   // 22 bits: a bound, not the exact key
+  const uint32_t k0 = ss.prefix;
+  __syncthreads();  // the sample area is reused for the candidates
+
+  const int nc = collect_candidates<NT>(row, L, aligned, k0, sm);
+  if (nc < k || nc > kCandCap) return false;
+  SelectState st{0u, 0u, k};
+  auto in_cand = [&](auto fn) {
+    for (int i = tid; i < nc; i += NT) fn(sm.c.ckey[i]);
+  };
+  int n_eq = refine_pass<NT>(st, 21, 11, in_cand, sm);
+  if (st.need != n_eq) n_eq = refine_pass<NT>(st, 10, 11, in_cand, sm);
+  if (st.need != n_eq) n_eq = refine_pass<NT>(st, 0, 10, in_cand, sm);
+  finish_candidates<NT>(L, k, st, n_eq, nc, out, sm);
+  return true;
+}
+
 // Top-k of a row streamed from global memory (k < L).
 template <int NT>
 __device__ __forceinline__ void select_row_stream(const float* __restrict__ row, int L, int k, int* __restrict__ out,
                                   SelectShared<NT>& sm) {
-  const int tid = threadIdx.x;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  if (L >= kSampleMinLen && L <= kBitmapWords * 32 && k <= kSampleMaxK &&
+      select_row_sampled<NT>(row, L, k, aligned, out, sm))
+    return;
 
   // 1. first digit
   int B1, above1, cnt1;
@@ -315,94 +483,19 @@ __device__ __forceinline__ void select_row_stream(const float* __restrict__ row,
     return;
   }
 
-  // 2. candidates (d1 >= B1) -> LDS: per-thread counts, one wave scan and
-  //    one reservation per wave and chunk
-  if (tid == 0) sm.bc[4] = 0;
-  __syncthreads();
-  {
-    constexpr int V = 8;
-    const uint32_t lo_key = static_cast<uint32_t>(B1) << kD1Shift;
-    const int lane = lane_id();
-    for (int base = 0; base < L; base += NT * 4 * V) {
-      uint32_t u[4 * V];
-      bool v[4 * V];
-      load_keys_strided<V, NT>(row, base, L, aligned, u, v);
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < 4 * V; ++j) c += (v[j] && u[j] >= lo_key) ? 1 : 0;
-      const int incl = wave_inclusive_scan(c);
-      const int wave_total = __shfl(incl, kWave - 1, kWave);
-      int wbase = 0;
-      if (lane == kWave - 1 && wave_total > 0) wbase = atomicAdd(&sm.bc[4], wave_total);
-      wbase = __shfl(wbase, kWave - 1, kWave);
-      int pos = wbase + incl - c;
-#pragma unroll
-      for (int j = 0; j < 4 * V; ++j) {
-        if (v[j] && u[j] >= lo_key) {
-          if (pos < kCandCap) {
-            sm.c.ckey[pos] = u[j];
-            sm.c.cidx[pos] = strided_pos<NT>(base, j);
-          }
-          ++pos;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const int nc = sm.bc[4];
+  // 2. candidates (d1 >= B1) -> LDS
+  const int nc = collect_candidates<NT>(row, L, aligned, static_cast<uint32_t>(B1) << kD1Shift, sm);
 
   // 3. exact threshold among the candidates of bin B1
   int n_eq = cnt1;
   if (st.need != cnt1) {
     n_eq = refine<NT>(st, 10, 10, 0, 10, [&](auto fn) {
-      for (int i = tid; i < nc; i += NT) fn(sm.c.ckey[i]);
+      for (int i = threadIdx.x; i < nc; i += NT) fn(sm.c.ckey[i]);
     }, sm);
   }
 
-  // 4. winners -> position bitmap
-  const int W = (L + 31) >> 5;
-  for (int j = tid; j < W; j += NT) sm.u.sel[j] = 0u;
-  __syncthreads();
-  const bool take_all_eq = st.need == n_eq;
-  for (int i = tid; i < nc; i += NT) {
-    const uint32_t m = sm.c.ckey[i] & st.pmask;
-    const int p = sm.c.cidx[i];
-    if (m > st.prefix || (take_all_eq && m == st.prefix)) atomicOr(&sm.u.sel[p >> 5], 1u << (p & 31));
-  }
-  if (!take_all_eq) {
-    // equal keys at the threshold: the `need` lowest positions among them,
-    // i.e. the largest of (2^17 - 1 - position), by radix select on 17 bits
-    const uint32_t tprefix = st.prefix, tmask = st.pmask;
-    SelectState ts{0u, 0u, st.need};
-    refine<NT>(ts, 8, 9, 0, 8, [&](auto fn) {
-      for (int i = tid; i < nc; i += NT)
-        if ((sm.c.ckey[i] & tmask) == tprefix) fn(0x1FFFFu - static_cast<uint32_t>(sm.c.cidx[i]));
-    }, sm);
-    for (int i = tid; i < nc; i += NT) {
-      const int p = sm.c.cidx[i];
-      if ((sm.c.ckey[i] & tmask) == tprefix && (0x1FFFFu - static_cast<uint32_t>(p)) >= ts.prefix)
-        atomicOr(&sm.u.sel[p >> 5], 1u << (p & 31));
-    }
-  }
-  __syncthreads();
-
-  // 5. ordered emission
-  const int wpt = (W + NT - 1) / NT;
-  const int w0 = tid * wpt;
-  const int w1 = (w0 + wpt < W) ? w0 + wpt : W;
-  int c_sel = 0;
-  for (int wd = w0; wd < w1; ++wd) c_sel += __popc(sm.u.sel[wd]);
-  int tot;
-  int pos = block_exclusive_scan<NT>(c_sel, tot, sm.scan);
-  for (int wd = w0; wd < w1; ++wd) {
-    uint32_t sel = sm.u.sel[wd];
-    while (sel) {
-      const int bpos = __builtin_ctz(sel);
-      sel &= sel - 1u;
-      out[pos++] = wd * 32 + bpos;
-    }
-  }
-  __syncthreads();
+  // 4, 5. winners -> position bitmap -> ordered emission
+  finish_candidates<NT>(L, k, st, n_eq, nc, out, sm);
 }
 
 // Top-k of a row held in registers (k < L <= kRowCap).  Thread t holds
@@ -452,7 +545,7 @@ __device__ __forceinline__ void select_row_reg(const float* __restrict__ row, in
     }
   }
   for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
-  block_min_max<NT>(lo, hi, sm.hist2);  // hist2 is free until the exact resolution
+  block_min_max<NT>(lo, hi, sm.hist2());  // hist2 is free until the exact resolution
   // bin(v) = clamp(fma(v, a, b), 0, 4095) truncated, with a = 4096 / (hi - lo)
   // and b = -lo a: one rounding of (v - lo) a, so monotone non-decreasing in
   // v.  (hi - lo is formed from halves so that it cannot overflow; when a or
@@ -602,6 +695,7 @@ __device__ __forceinline__ void select_row_reg(const float* __restrict__ row, in
 // workgroups per CU.
 template <int NT, bool kReg = true>
 __device__ __forceinline__ void select_row(const float* __restrict__ row, int L, int k, int* __restrict__ out, SelectShared<NT>& sm) {
+  static_assert(!(kReg && SelectShared<NT>::kShareHist2), "the register path needs its own second-digit histogram");
   if (L <= k) {
     for (int j = threadIdx.x; j < k; j += NT) out[j] = (j < L) ? j : -1;
   } else if (kReg && L <= kRowCap) {
