@@ -330,10 +330,10 @@ def run_decode(wl, args, pools=None) -> dict:
 
     dev = torch.device("cuda:0")
     copies = args.copies if args.copies else DEFAULT_COPIES.get(wl.name, 2)
-    pools = [torch.from_numpy(wl.cache).to(dev)]
+    pool_copies = [torch.from_numpy(wl.cache).to(dev)]
     for _ in range(copies - 1):
-        pools.append(pools[0].clone())
-    caches = [idx.Cache(p, wl.head_dim, wl.fmt, wl.page_size) for p in pools]
+        pool_copies.append(pool_copies[0].clone())
+    caches = [idx.Cache(p, wl.head_dim, wl.fmt, wl.page_size) for p in pool_copies]
     bt = torch.from_numpy(wl.block_table).to(dev)
     seq = torch.from_numpy(wl.seq_lens).to(dev)
     dl = None if wl.decode_lens is None else torch.from_numpy(wl.decode_lens).to(dev)
@@ -427,7 +427,7 @@ def run_decode(wl, args, pools=None) -> dict:
         "whole_step": {"algorithmic_bytes": ab["step"], "achieved": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
                        "achieved_graph": graph_gbs, "frac_graph": graph_gbs / HBM_PEAK_GBS, "unit": "GB/s"},
     }
-    del pools, caches, logits, outs, sep, ws, g
+    del pool_copies, caches, logits, outs, sep, ws, g
     torch.cuda.empty_cache()
     return res
 

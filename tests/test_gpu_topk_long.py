@@ -108,3 +108,32 @@ def test_rows_past_bitmap_lean_batch(k):
     for r, v in enumerate(vals):
         exp = oracle.topk.topk_row(v.astype(np.float64), lens[r], k)
         assert np.array_equal(got[r], exp), f"row {r} (L={lens[r]}, pattern {r % 9}) differs"
+
+
+@pytest.mark.parametrize("k", [1, 64, 2048])
+def test_sampled_selection_skewed_samples(k):
+    """Rows whose systematic block sample (every 16th 64-key block for these
+    lengths) misjudges the threshold: large values exactly on the sampled
+    blocks (too few keys reach the sample's threshold) or small values there
+    (too many): the one-read selection falls back, the rows stay exact;
+    plus ordinary rows that take the one-read path.  512 rows: the
+    streaming-only kernel."""
+    rng = np.random.default_rng(3000 + k)
+    R = 512
+    lens, vals = [], []
+    for r in range(R):
+        L = [65536, 40000, 16384, 20000][r % 4]
+        v = rng.standard_normal(L).astype(np.float32)
+        blocks = np.arange(L) // 64
+        on = blocks % 16 == 0
+        kind = r % 3
+        if kind == 0:
+            v[on] = 100.0 + rng.random(on.sum()).astype(np.float32)
+        elif kind == 1:
+            v[on] = -100.0 - rng.random(on.sum()).astype(np.float32)
+        lens.append(L)
+        vals.append(v)
+    got = _run_rows(lens, vals, k)
+    for r, v in enumerate(vals):
+        exp = oracle.topk.topk_row(v.astype(np.float64), lens[r], k)
+        assert np.array_equal(got[r], exp), f"row {r} (L={lens[r]}, kind {r % 3}) differs"
