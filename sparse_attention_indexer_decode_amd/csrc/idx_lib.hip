@@ -164,7 +164,11 @@ size_t decode_ws_bytes(const RowArgs& R) {
 
 template <int D, bool MX, int MT>
 hipError_t launch_score(const ScoreParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((score_kernel<D, MX, MT>), dim3(grid), dim3(kDecodeWaves * kWave), 0, s, p);
+  // next_n = 2: the two rows of a request on a wave pair
+  if (p.rows.next_n == 2)
+    hipLaunchKernelGGL((score_kernel<D, MX, MT, true>), dim3(grid), dim3(kDecodeWaves * kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL((score_kernel<D, MX, MT, false>), dim3(grid), dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 

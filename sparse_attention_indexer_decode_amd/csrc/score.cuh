@@ -544,6 +544,85 @@ __device__ __forceinline__ int page_ids(const ScoreParams& p, const int* page_pr
   return ok ? (e << sh) | (u & ((1 << sh) - 1)) : -1;  // unit id, or -1 outside the pool
 }
 
+// ---------------------------------------------------------------------------
+// Requests of two grid rows (next_n = 2): wave pairs
+// ---------------------------------------------------------------------------
+//
+// With one row per wave over a list of rows, the two rows of a request read
+// its pages on unrelated waves at unrelated times, and the second read goes
+// past L2 (measured: 1.48x the key bytes fetched on the MTP decode batch).
+// For next_n = 2 the list counts request units instead, and each pair of
+// waves of a workgroup (waves 2m and 2m + 1: one CU, so one L2) walks one
+// contiguous range of them.  A request with two real rows has one unit per
+// 64-key unit of its longer row, and the pair scores rows 0 and 1 of the same
+// unit side by side, so the second request for a page finds it in the L2
+// the first one filled; a request with one real row has one unit per two of
+// its 64-key units, one for each wave.
+
+// (request keys clamped to max_len, real rows) of request b.
+__device__ __forceinline__ void pair_request(const RowArgs& R, int b, int& seq, int& dl) {
+  seq = R.seq_lens[b];
+  seq = seq > R.max_len ? R.max_len : seq;
+  dl = R.decode_lens ? R.decode_lens[b] : 2;
+}
+
+// 64-key units of row 0 of a one-row request.
+__device__ __forceinline__ int pair_row0_units(const RowArgs& R, int seq) {
+  return (decode_row_len(seq, 1, 0, R.max_len, R.ratio) + kPage - 1) / kPage;
+}
+
+// Units of request b in the pair list.
+__device__ __forceinline__ int pair_units(const RowArgs& R, int b) {
+  int seq, dl;
+  pair_request(R, b, seq, dl);
+  if (dl >= 2) return (decode_row_len(seq, dl, 1, R.max_len, R.ratio) + kPage - 1) / kPage;
+  if (dl == 1) return (pair_row0_units(R, seq) + 1) / 2;
+  return 0;
+}
+
+// 64-key unit that the wave of parity `par` scores at unit t of a request
+// with `dl` real rows (`np0` units in row 0 when dl = 1), or -1.
+__device__ __forceinline__ int pair_unit(int dl, int np0, int t, int par) {
+  if (dl >= 2) return t;
+  const int u = 2 * t + par;
+  return u < np0 ? u : -1;
+}
+
+// Units per request -> exclusive prefix in sm.page_prefix[0 .. num_req].
+template <int NT, class SM>
+__device__ __forceinline__ void build_pair_prefix(const RowArgs& R, SM& sm) {
+  const int tid = threadIdx.x;
+  int run = 0;
+  for (int base = 0; base < R.num_req; base += NT) {
+    const int b = base + tid;
+    const int n = b < R.num_req ? pair_units(R, b) : 0;
+    int tot;
+    const int ex = block_exclusive_scan<NT>(n, tot, sm.misc);
+    if (b < R.num_req) sm.page_prefix[b] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) sm.page_prefix[R.num_req] = run;
+  __syncthreads();
+}
+
+// page_ids for the pair list: unit ids of the pages of units jb + lane for
+// the wave of parity par; -2 where this wave has no page (a one-row
+// request's odd last unit), -1 outside the pool.
+__device__ __forceinline__ int pair_page_ids(const ScoreParams& p, const int* page_prefix, int jb, int j1, int par) {
+  const int j = jb + lane_id();
+  if (j >= j1) return 0;
+  const RowArgs& R = p.rows;
+  const int b = group_of_page(page_prefix, R.num_req, j);
+  int seq, dl;
+  pair_request(R, b, seq, dl);
+  const int u = pair_unit(dl, dl == 1 ? pair_row0_units(R, seq) : 0, j - page_prefix[b], par);
+  if (u < 0) return -2;
+  const int sh = p.cache.page_shift;
+  const int e = R.block_table[static_cast<int64_t>(b) * R.bt_stride + (u >> sh)];
+  const bool ok = e >= 0 && static_cast<int64_t>(e) < p.cache.num_pages;
+  return ok ? (e << sh) | (u & ((1 << sh) - 1)) : -1;
+}
+
 // The row of group g (decode groups hold one row): its query fragments,
 // head weights (through the wave's LDS staging row, into the accumulator
 // layout) and output descriptor.  `stage` is the wave's idle LDS area for a
@@ -585,10 +664,10 @@ __device__ __forceinline__ int setup_row(const ScoreParams& p, const int (*req_t
   return __builtin_amdgcn_readfirstlane(Lr);
 }
 
-// Decode scorer: every decode row is a group of its own (the next_n rows of
-// a request read the request's pages separately; their waves run at the
-// same time, so the second read mostly hits the caches).
-template <int D, bool MX, int MT>
+// Decode scorer: every decode row is a group of its own and every wave walks
+// a contiguous range of the list of rows' pages; with PAIRS (next_n = 2)
+// the list counts request units and wave pairs walk it (see above).
+template <int D, bool MX, int MT, bool PAIRS>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScoreParams p) {
   constexpr int kThreads = kDecodeWaves * kWave;
   __shared__ ScoreShared<D, MX, MT, kDecodeWaves> sm;
@@ -599,14 +678,23 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
   const bool tables = R.kind != 0 || R.q_packed;
   const int NG = tables ? build_request_tables<1, kThreads>(R, sm) : p.num_groups;
 
-  build_page_prefix<1, kThreads>(R, sm, NG);
-  const int P = sm.page_prefix[NG];
-
-  // this wave's contiguous page range
+  int NL;  // entries of the list: rows, or requests with PAIRS
   int j0, j1;
-  even_split(P, gridDim.x * kDecodeWaves, blockIdx.x * kDecodeWaves + wave, j0, j1);
+  if constexpr (PAIRS) {
+    build_pair_prefix<kThreads>(R, sm);
+    NL = R.num_req;
+    // this wave pair's contiguous unit range
+    even_split(sm.page_prefix[NL], gridDim.x * (kDecodeWaves / 2), blockIdx.x * (kDecodeWaves / 2) + (wave >> 1),
+               j0, j1);
+  } else {
+    build_page_prefix<1, kThreads>(R, sm, NG);
+    NL = NG;
+    // this wave's contiguous page range
+    even_split(sm.page_prefix[NL], gridDim.x * kDecodeWaves, blockIdx.x * kDecodeWaves + wave, j0, j1);
+  }
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
+  const int par = wave & 1;
 
   float* wrow = sm.wbuf[wave];
   WaveArea<D, MX, MT>& area = sm.area[wave];
@@ -616,31 +704,48 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
 
   bool bad_page = false;
   if (j0 < j1) {
-    // Page ids come in batches of 64 (lane i: page jb + i), so that no
+    // Page ids come in batches of 64 (lane i: entry jb + i), so that no
     // compiler-visible load sits between page requests; a later batch costs
     // one drain of the requests in flight.
+    auto batch = [&](int jb_) -> int {
+      if constexpr (PAIRS) return pair_page_ids(p, sm.page_prefix, jb_, j1, par);
+      else return page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb_, j1);
+    };
     int jb = j0;
-    int ids = page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+    int ids = batch(jb);
     auto id_of = [&](int j) -> int {  // j < j1
       if (j - jb >= kWave) {
         jb = j;
-        ids = page_ids<1>(p, sm.page_prefix, sm.req_tab, NG, jb, j1);
+        ids = batch(jb);
       }
       const int id = __builtin_amdgcn_readlane(ids, j - jb);
-      const bool ok = id >= 0;
-      bad_page |= !ok;  // ids outside the pool read page 0 and are reported
-      return ok ? id : 0;
+      bad_page |= id == -1;  // ids outside the pool read page 0 and are reported
+      return id >= 0 ? id : 0;  // (-2: no page for this wave; page 0 keeps the ring moving)
     };
 
-    // The first group's queries and weights are loaded together with the
+    // The row this wave scores in list entry g, and with PAIRS the request's
+    // real rows and row-0 units.
+    int dl_cur = 0, np0_cur = 0;
+    auto entry_row = [&](int g) -> int {
+      if constexpr (PAIRS) {
+        int seq;
+        pair_request(R, g, seq, dl_cur);
+        np0_cur = dl_cur == 1 ? pair_row0_units(R, seq) : 0;
+        return 2 * g + (dl_cur >= 2 ? par : 0);
+      } else {
+        return g;
+      }
+    };
+
+    // The first entry's queries and weights are loaded together with the
     // ids and before any page is requested: waiting for them then never
     // waits for a page, and the first page can be scored as soon as it lands.
     QFrag<D, MT> qf;
     WFrag<MT> wf;
     RowOut out;
-    int gs = group_of_page(sm.page_prefix, NG, j0);  // group of the page being scored
-    int row_len = setup_row<D, MT>(p, sm.req_tab, gs, wrow, qf, wf, out, area.stage);
-    int g_first = sm.page_prefix[gs];  // the group's first global page
+    int gs = group_of_page(sm.page_prefix, NL, j0);  // list entry of the page being scored
+    int row_len = setup_row<D, MT>(p, sm.req_tab, entry_row(gs), wrow, qf, wf, out, area.stage);
+    int g_first = sm.page_prefix[gs];  // the entry's first list index
     int cur_g = gs;
 
     int first[NP];
@@ -665,21 +770,24 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
     for (int j = j0; j < j1; ++j) {
       gs = advance_group(sm.page_prefix, gs, j);
       if (gs != cur_g) {
-        // a later group (waiting for its loads drains the page requests in
-        // flight; a wave's range crosses few group boundaries)
-        tile_logits<MT>(acc1, ks1, wf, out, off1);  // the old group's pending tile
+        // a later entry (waiting for its loads drains the page requests in
+        // flight; a wave's range crosses few entry boundaries)
+        tile_logits<MT>(acc1, ks1, wf, out, off1);  // the old row's pending tile
         off1 = 0x7FFFFFF0;
-        row_len = setup_row<D, MT>(p, sm.req_tab, gs, wrow, qf, wf, out, nullptr);
+        row_len = setup_row<D, MT>(p, sm.req_tab, entry_row(gs), wrow, qf, wf, out, nullptr);
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
+      // the row's 64-key unit at list index j (none for this wave: -1)
+      int u = j - g_first;
+      if constexpr (PAIRS) u = pair_unit(dl_cur, np0_cur, u, par);
       const int nxt = j + NP < j1 ? id_of(j + NP) : 0;
       // page j has landed once only the requests after it (pages up to
       // j + NP - 1) are outstanding
       wait_page_with_later<D, MX>((j + NP - 1 < j1 - 1 ? j + NP - 1 : j1 - 1) - j);
-      if (row_len > 0) {  // wave-uniform: a padded slot only keeps the ring moving
+      if (row_len > 0 && u >= 0) {  // wave-uniform: a padded slot only keeps the ring moving
         const uint8_t* buf = area.page[slot];
-        const int base = (j - g_first) * kPage * 4 + key_off;
+        const int base = u * kPage * 4 + key_off;
         tile_mfma_raw<D, MX, MT>(buf, 0, qf, acc0, ks0);
         tile_logits<MT>(acc1, ks1, wf, out, off1);
         __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
