@@ -101,11 +101,14 @@ def kernel_source_hash() -> str:
 
 
 def scorer_kernel_name(wl) -> str:
-    """The dominant kernel's name as rocprofv3 prints it."""
+    """The dominant kernel's name as rocprofv3 prints it (decode: the last
+    template argument is the wave-pair form used for next_n = 2)."""
     mt = 2 if wl.heads > 32 else 1
     mx = "true" if wl.fmt == "mxfp4" else "false"
-    kern = "score_block_kernel" if wl.kind == "prefill" else "score_kernel"
-    return f"{kern}<{wl.head_dim}, {mx}, {mt}>"
+    if wl.kind == "prefill":
+        return f"score_block_kernel<{wl.head_dim}, {mx}, {mt}>"
+    pairs = "true" if wl.next_n == 2 else "false"
+    return f"score_kernel<{wl.head_dim}, {mx}, {mt}, {pairs}>"
 
 
 # ---------------------------------------------------------------------------

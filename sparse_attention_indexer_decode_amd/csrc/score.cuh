@@ -467,6 +467,28 @@ __device__ __forceinline__ void tile_logits(const v16f (&acc)[MT], float key_sca
   finish_key(ps, key_scale, out, (lane_id() >> 5) == 0 ? off : 0x7FFFFFF0);
 }
 
+// Weighted ReLU head sum of one 32-key tile into one partial per lane (this
+// lane half's heads of key lane % 32), in two independent chains.
+template <int MT>
+__device__ __forceinline__ float tile_partial(const v16f (&acc)[MT], const WFrag<MT>& wf) {
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) head_sum<MT>(acc[mt], wf, mt, ps);
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// Logits of a page's 64 keys from the partials of its two tiles: one swap of
+// lane halves (v_permlane32_swap: lanes 32..63 of the first operand with
+// lanes 0..31 of the second) leaves tile 0's totals in lanes 0..31 and tile
+// 1's in lanes 32..63, i.e. key `lane` of the page in lane `lane`; times that
+// key's fp8 scale, stored at byte offset off + 4 lane (off: the page's first
+// key in the row; out of range: nothing stored).
+__device__ __forceinline__ void page_logits(float p0, float p1, float key_scale, const RowOut& out, int off) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * key_scale;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out, off + 4 * lane_id(), 0, 0);
+}
+
 constexpr int kBlockRows = 8;  // rows per group = waves per workgroup
 constexpr int kRing = 4;       // page buffers per workgroup
 
@@ -835,14 +857,11 @@ __device__ __forceinline__ void decode_page_slice(const uint8_t* raw, v8bf* dec,
   }
 }
 
-// Raw scores of one row against 32-key tile nt of a decoded page (fp8 token
-// scales from the raw page).
+// Raw scores of one row against 32-key tile nt of a decoded page.
 template <int D, bool MX, int MT>
-__device__ __forceinline__ void tile_mfma(const v8bf* dec, const uint8_t* raw, int nt, const QFrag<D, MT>& qf,
-                                          v16f (&acc)[MT], float& key_scale) {
+__device__ __forceinline__ void tile_mfma(const v8bf* dec, int nt, const QFrag<D, MT>& qf, v16f (&acc)[MT]) {
   constexpr int KS = D / 16;
   const int lane = lane_id();
-  key_scale = MX ? 1.0f : *reinterpret_cast<const float*>(raw + (nt * 32 + (lane & 31)) * Geometry<D, MX>::kRowBytes + D);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = v16f{};
 #pragma unroll
@@ -961,15 +980,18 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
   // of the tile before it (independent work the SIMD overlaps), alternating
   // between two accumulator sets.  The range is walked one group at a time,
   // so that setting up a row stays out of the page loop.
-  const int key_off = (lane & 31) * 4;
+  // The two tiles of a page are finished together (page_logits), one page
+  // behind: tile 0's partial waits in a register for tile 1's.
+  constexpr int kNone = 0x7FFFFF00;  // an offset past any row: nothing stored
   v16f acc0[MT], acc1[MT];
-  float ks0 = 0.0f, ks1 = 0.0f;
   int j = j0;
   for (;;) {
     const int seg_end = sm.page_prefix[gs + 1] < j1 ? sm.page_prefix[gs + 1] : j1;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc1[mt] = v16f{};
-    int off1 = 0x7FFFFFF0;  // byte offset of the pending tile 1 (none yet)
+    float pend0 = 0.0f;     // tile 0 partial of the pending page
+    float pend_ks = 0.0f;   // its key scales (key `lane` of the page)
+    int pend_off = kNone;   // its first key's byte offset in the row (none yet)
     for (; j < seg_end; ++j) {
       const int i = j - j0;  // page j0 + i sits in raw buffer i % kRing, decoded buffer i % 2
       if (issuer && j + 1 < j1) {
@@ -983,18 +1005,19 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
       }
       const v8bf* dec = sm.dec[i & 1];
       const uint8_t* raw = sm.ring[i % kRing];
-      const int base = (j - g_first) * kPage * 4 + key_off;
-      tile_mfma<D, MX, MT>(dec, raw, 0, qf, acc0, ks0);
-      tile_logits<MT>(acc1, ks1, wf, out, off1);
+      const float ks = MX ? 1.0f : *reinterpret_cast<const float*>(raw + lane * Geometry<D, MX>::kRowBytes + D);
+      tile_mfma<D, MX, MT>(dec, 0, qf, acc0);
+      page_logits(pend0, tile_partial<MT>(acc1, wf), pend_ks, out, pend_off);  // the previous page
       __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
       if (j + 1 < j1) decode_page_slice<D, MX>(sm.ring[(i + 1) % kRing], sm.dec[(i + 1) & 1], wave);
       __builtin_amdgcn_sched_barrier(0);
-      tile_mfma<D, MX, MT>(dec, raw, 1, qf, acc1, ks1);
-      tile_logits<MT>(acc0, ks0, wf, out, base);
+      tile_mfma<D, MX, MT>(dec, 1, qf, acc1);
+      pend0 = tile_partial<MT>(acc0, wf);
       __builtin_amdgcn_sched_barrier(0);
-      off1 = base + 32 * 4;
+      pend_ks = ks;
+      pend_off = (j - g_first) * kPage * 4;
     }
-    tile_logits<MT>(acc1, ks1, wf, out, off1);  // the segment's last tile
+    page_logits(pend0, tile_partial<MT>(acc1, wf), pend_ks, out, pend_off);  // the segment's last page
     if (j >= j1) break;
     gs = advance_group(sm.page_prefix, gs, j);
     setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
