@@ -325,6 +325,18 @@ def capture(fn, n_inner: int):
 # Decode and prefill runs
 # ---------------------------------------------------------------------------
 
+def calib_copy(args, dev) -> None:
+    """A plain elementwise copy of known size, for scaling the HBM counters."""
+    import torch
+
+    src = torch.ones((args.calib_mib << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_decode(wl, args, pools=None) -> dict:
     import numpy as np
     import torch
@@ -370,12 +382,7 @@ def run_decode(wl, args, pools=None) -> dict:
             idx.idx_topk(logits, rows, k, out, ws)
 
     if args.calib:
-        src = torch.ones((args.calib_mib << 20) // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(args, dev)
 
     for i in range(args.warmup):
         step(i)
@@ -468,6 +475,8 @@ def run_prefill(wl, args) -> dict:
                        idx.idx_workspace_bytes(idx.IDX_OP_TOPK, None, c[0], 0, k)) for c in chunks)
     ws = idx.new_workspace(ws_bytes, dev)
     stream = torch.cuda.current_stream()
+    if args.calib:
+        calib_copy(args, dev)
 
     def score(ci):
         r, qq, ww, M, N = chunks[ci]
