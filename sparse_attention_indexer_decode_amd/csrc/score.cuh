@@ -491,6 +491,7 @@ __device__ __forceinline__ void page_logits(float p0, float p1, float key_scale,
 
 constexpr int kBlockRows = 8;  // rows per group = waves per workgroup
 constexpr int kRing = 4;       // page buffers per workgroup
+constexpr int kDecBufs = 3;    // decoded pages: the one scored, the next, the one being decoded
 
 template <int D, bool MX>
 struct BlockShared {
@@ -499,7 +500,7 @@ struct BlockShared {
   float wbuf[kBlockRows][kMaxHeads];
   int misc[16];
   alignas(16) uint8_t ring[kRing][Geometry<D, MX>::kPageBytes];  // raw pages
-  alignas(16) v8bf dec[2][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
+  alignas(16) v8bf dec[kDecBufs][2 * (D / 16) * kWave];  // decoded pages, in B-fragment order
 };
 
 // ---------------------------------------------------------------------------
@@ -835,9 +836,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
 // one key per row, so here a group is kBlockRows consecutive query rows and
 // each wave scores one of them: every page is read from memory once per
 // group and shared by the eight waves through a ring of kRing page buffers
-// in LDS.  Wave 0 requests pages kRing - 1 ahead.  Each page is decoded to
-// bf16 once, by all waves together (an eighth each), into one of two
-// decoded-page buffers, so that the per-row VALU work is the head sums.
+// in LDS.  Wave 0 requests pages four ahead of the one scored.  Each page
+// is decoded to bf16 once, by all waves together (an eighth each), two pages
+// ahead of scoring, into one of kDecBufs decoded-page buffers, so that the
+// per-row VALU work is the head sums.
 
 // Decodes this wave's share of a raw page into B-fragment order: fragment
 // (tile nt, k-step s) of lane l goes to dec[(nt KS + s) 64 + l], so that a
@@ -850,7 +852,7 @@ __device__ __forceinline__ void decode_page_slice(const uint8_t* raw, v8bf* dec,
 #pragma unroll
   for (int b0 = 0; b0 < 2 * KS; b0 += kBlockRows) {
     const int blk = b0 + wave;
-    if (blk < 2 * KS) {
+    if ((2 * KS) % kBlockRows == 0 || blk < 2 * KS) {
       const int nt = blk / KS, s = blk % KS;
       dec[blk * kWave + lane] = key_step<D, MX>(raw + (nt * 32 + (lane & 31)) * Geometry<D, MX>::kRowBytes, lane >> 5, s);
     }
@@ -917,9 +919,37 @@ __device__ __forceinline__ void wait_ring_page(int after) {
   else wait_all_loads();
 }
 
+// A tile's B fragments, read from a decoded page into registers.
+template <int D>
+__device__ __forceinline__ void tile_frags(const v8bf* dec, int nt, v8bf (&b)[D / 16]) {
+  constexpr int KS = D / 16;
+  const int lane = lane_id();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) b[s] = dec[(nt * KS + s) * kWave + lane];
+}
+
+template <int D, int MT>
+__device__ __forceinline__ void tile_mfma_regs(const v8bf (&b)[D / 16], const QFrag<D, MT>& qf, v16f (&acc)[MT]) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v16f{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf.a[mt][s], b[s], acc[mt], 0, 0, 0);
+}
+
+// Key scale of key `lane` of a raw page (fp8 rows carry one; MXFP4 block
+// scales are applied while decoding).
+template <int D, bool MX>
+__device__ __forceinline__ float raw_key_scale(const uint8_t* raw) {
+  return MX ? 1.0f : *reinterpret_cast<const float*>(raw + lane_id() * Geometry<D, MX>::kRowBytes + D);
+}
+
 template <int D, bool MX, int MT>
 __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(ScoreParams p) {
   constexpr int NT = kBlockRows * kWave;
+  constexpr int KS = D / 16;
   __shared__ BlockShared<D, MX> sm;
   const RowArgs& R = p.rows;
   const int tid = threadIdx.x;
@@ -958,30 +988,39 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
   setup_block_row<D, MT>(p, sm.req_tab, gs, wave, sm.wbuf[wave], qf, wf, out);
   int g_first = sm.page_prefix[gs];
 
+  // Pipeline (page j0 + i: raw buffer i % kRing, decoded buffer i % kDecBufs):
+  // in the iteration of page j the waves score page j, decode page j + 2
+  // and read the first tile's fragments of page j + 1 (decoded two
+  // iterations before), and wave 0 requests page j + 4; one barrier per
+  // page, at the end, publishes decoded page j + 2 and raw page j + 3 and
+  // retires every read of page j - 1's buffers.  The first tile's
+  // fragments are thus in registers when the barrier opens, and the decode
+  // runs under the MFMAs of page j.
   if (issuer) {
-    int first[kRing - 1];
+    int first[kRing];
 #pragma unroll
-    for (int i = 0; i < kRing - 1; ++i) first[i] = j0 + i < j1 ? id_of(j0 + i) : 0;
+    for (int i = 0; i < kRing; ++i) first[i] = j0 + i < j1 ? id_of(j0 + i) : 0;
     wait_all_loads();  // nothing the compiler loaded before is still in flight
 #pragma unroll
-    for (int i = 0; i < kRing - 1; ++i)
+    for (int i = 0; i < kRing; ++i)
       if (j0 + i < j1) dma_page<D, MX>(p, first[i], lds_addr(sm.ring[i]));
-    wait_ring_page<D, MX>((j0 + kRing - 2 < j1 - 1 ? j0 + kRing - 2 : j1 - 1) - j0);  // page j0 has landed
+    // pages j0 and j0 + 1 have landed
+    const int last = j0 + kRing - 1 < j1 - 1 ? j0 + kRing - 1 : j1 - 1;
+    wait_ring_page<D, MX>(last - (j0 + 1) > 0 ? last - (j0 + 1) : 0);
   }
   __syncthreads();
   decode_page_slice<D, MX>(sm.ring[0], sm.dec[0], wave);
+  float ks_cur = raw_key_scale<D, MX>(sm.ring[0]);
+  float ks_nxt = 0.0f;
+  if (j0 + 1 < j1) {
+    decode_page_slice<D, MX>(sm.ring[1], sm.dec[1], wave);
+    ks_nxt = raw_key_scale<D, MX>(sm.ring[1]);
+  }
+  if (issuer && j0 + 2 < j1) wait_ring_page<D, MX>(j0 + 3 < j1 ? 1 : 0);  // page j0 + 2 has landed
+  __syncthreads();
+  v8bf bt0[KS];
+  tile_frags<D>(sm.dec[0], 0, bt0);
 
-  // Per page j: one barrier publishes raw page j + 1 and decoded page j and
-  // frees the buffers of page j - 1; then page j + kRing - 1 is requested
-  // and page j scored, with page j + 1 decoded between its two tiles (so the
-  // decode's LDS round trip runs under the first tile's MFMAs instead of
-  // stalling every wave right after the barrier).  Scoring is software-pipelined
-  // over 32-key tiles: the MFMAs of a tile are issued next to the head sums
-  // of the tile before it (independent work the SIMD overlaps), alternating
-  // between two accumulator sets.  The range is walked one group at a time,
-  // so that setting up a row stays out of the page loop.
-  // The two tiles of a page are finished together (page_logits), one page
-  // behind: tile 0's partial waits in a register for tile 1's.
   constexpr int kNone = 0x7FFFFF00;  // an offset past any row: nothing stored
   v16f acc0[MT], acc1[MT];
   int j = j0;
@@ -993,29 +1032,35 @@ __global__ __launch_bounds__(kBlockRows * kWave, 1) void score_block_kernel(Scor
     float pend_ks = 0.0f;   // its key scales (key `lane` of the page)
     int pend_off = kNone;   // its first key's byte offset in the row (none yet)
     for (; j < seg_end; ++j) {
-      const int i = j - j0;  // page j0 + i sits in raw buffer i % kRing, decoded buffer i % 2
-      if (issuer && j + 1 < j1) {
-        const int last = j + kRing - 2 < j1 - 1 ? j + kRing - 2 : j1 - 1;
-        wait_ring_page<D, MX>(last - (j + 1));  // raw page j + 1 has landed
+      const int i = j - j0;
+      if (issuer && j + kRing < j1) {
+        const int nxt = id_of(j + kRing);
+        dma_page<D, MX>(p, nxt, lds_addr(sm.ring[i % kRing]));
       }
-      __syncthreads();
-      if (issuer && j + kRing - 1 < j1) {
-        const int nxt = id_of(j + kRing - 1);
-        dma_page<D, MX>(p, nxt, lds_addr(sm.ring[(i + kRing - 1) % kRing]));
+      const v8bf* dec = sm.dec[i % kDecBufs];
+      float ks_new;
+      {
+        // past the range's end this decodes a stale buffer into a decoded
+        // buffer that nothing reads again (branch-free, so that the decode
+        // interleaves with the MFMAs)
+        const uint8_t* raw2 = sm.ring[(i + 2) % kRing];
+        decode_page_slice<D, MX>(raw2, sm.dec[(i + 2) % kDecBufs], wave);
+        ks_new = raw_key_scale<D, MX>(raw2);
       }
-      const v8bf* dec = sm.dec[i & 1];
-      const uint8_t* raw = sm.ring[i % kRing];
-      const float ks = MX ? 1.0f : *reinterpret_cast<const float*>(raw + lane * Geometry<D, MX>::kRowBytes + D);
-      tile_mfma<D, MX, MT>(dec, 0, qf, acc0);
+      tile_mfma_regs<D, MT>(bt0, qf, acc0);
       page_logits(pend0, tile_partial<MT>(acc1, wf), pend_ks, out, pend_off);  // the previous page
       __builtin_amdgcn_sched_barrier(0);  // keep each stage's registers to itself
-      if (j + 1 < j1) decode_page_slice<D, MX>(sm.ring[(i + 1) % kRing], sm.dec[(i + 1) & 1], wave);
-      __builtin_amdgcn_sched_barrier(0);
       tile_mfma<D, MX, MT>(dec, 1, qf, acc1);
       pend0 = tile_partial<MT>(acc0, wf);
+      tile_frags<D>(sm.dec[(i + 1) % kDecBufs], 0, bt0);  // (stale past the end, unused)
+      __asm__ volatile("" : : "v"(pend0), "v"(ks_new));  // computed here, not after the wait below
       __builtin_amdgcn_sched_barrier(0);
-      pend_ks = ks;
+      pend_ks = ks_cur;
+      ks_cur = ks_nxt;
+      ks_nxt = ks_new;
       pend_off = (j - g_first) * kPage * 4;
+      if (issuer && j + 3 < j1) wait_ring_page<D, MX>(j + kRing < j1 ? 1 : 0);  // raw page j + 3 has landed
+      __syncthreads();
     }
     page_logits(pend0, tile_partial<MT>(acc1, wf), pend_ks, out, pend_off);  // the segment's last page
     if (j >= j1) break;
