@@ -45,6 +45,16 @@ __device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uin
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
 }
+// The same two with the non-temporal hint (data read once: the caches need
+// not keep it).
+__device__ __forceinline__ void lds_dma16_s_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_s_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS byte address of a shared-memory pointer.

@@ -370,8 +370,8 @@ __device__ __forceinline__ void key_fragments(const uint8_t* rowp, int g, v8bf (
 
 // Requests 64-key unit `phys` (see page_ids) into the LDS buffer at byte
 // address `lds`: byte i of the unit lands at lds + i.  Always issues exactly
-// kLoads loads.
-template <int D, bool MX>
+// kLoads loads.  ONCE: the unit is read once per launch (non-temporal hint).
+template <int D, bool MX, bool ONCE = false>
 __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_t lds) {
   using Geo = Geometry<D, MX>;
   const int lane = lane_id();
@@ -379,10 +379,15 @@ __device__ __forceinline__ void dma_page(const ScoreParams& p, int phys, uint32_
   const uint8_t* src = p.cache.base + static_cast<int64_t>(phys >> sh) * p.cache.page_bytes +
                        (phys & ((1 << sh) - 1)) * Geo::kPageBytes;
 #pragma unroll
-  for (int c = 0; c < Geo::kWide; ++c) lds_dma16_s(src + 1024 * c, 16 * lane, lds + 1024 * c);
+  for (int c = 0; c < Geo::kWide; ++c) {
+    if constexpr (ONCE) lds_dma16_s_nt(src + 1024 * c, 16 * lane, lds + 1024 * c);
+    else lds_dma16_s(src + 1024 * c, 16 * lane, lds + 1024 * c);
+  }
 #pragma unroll
-  for (int c = 0; c < Geo::kNarrow; ++c)
-    lds_dma4_s(src + 1024 * Geo::kWide + 256 * c, 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
+  for (int c = 0; c < Geo::kNarrow; ++c) {
+    if constexpr (ONCE) lds_dma4_s_nt(src + 1024 * Geo::kWide + 256 * c, 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
+    else lds_dma4_s(src + 1024 * Geo::kWide + 256 * c, 4 * lane, lds + 1024 * Geo::kWide + 256 * c);
+  }
 }
 
 // Waits until a page has landed in LDS, given how many pages were requested
@@ -771,6 +776,14 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
     int g_first = sm.page_prefix[gs];  // the entry's first list index
     int cur_g = gs;
 
+    // With one row per request every page is read once per launch: its
+    // requests carry the non-temporal hint (rows of one request read their
+    // pages again and keep the default).
+    const bool once = !PAIRS && R.next_n == 1;
+    auto request = [&](int id, uint32_t lds) {
+      if (once) dma_page<D, MX, true>(p, id, lds);
+      else dma_page<D, MX, false>(p, id, lds);
+    };
     int first[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) first[i] = j0 + i < j1 ? id_of(j0 + i) : 0;
@@ -778,7 +791,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
     wait_lds();        // the staged query reads have returned: the area is free
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-      if (j0 + i < j1) dma_page<D, MX>(p, first[i], ring_lds + i * Geometry<D, MX>::kPageBytes);
+      if (j0 + i < j1) request(first[i], ring_lds + i * Geometry<D, MX>::kPageBytes);
 
     int slot = 0;  // ring slot of page j
     // 32-key tiles are pipelined across pages: a tile's MFMAs are issued
@@ -798,6 +811,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
         tile_logits<MT>(acc1, ks1, wf, out, off1);  // the old row's pending tile
         off1 = 0x7FFFFFF0;
         row_len = setup_row<D, MT>(p, sm.req_tab, entry_row(gs), wrow, qf, wf, out, nullptr);
+        // Wait for the new row's loads here, on this path only.  Left to the
+        // compiler, the waits for them land at their first uses in the
+        // scoring below, which runs for every page, where they also count
+        // the page requests in flight (the compiler does not see those).
+        wait_all_loads();
         g_first = sm.page_prefix[gs];
         cur_g = gs;
       }
@@ -819,7 +837,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void score_kernel(ScorePar
         __builtin_amdgcn_sched_barrier(0);
         off1 = base + 32 * 4;
       }
-      if (j + NP < j1) dma_page<D, MX>(p, nxt, ring_lds + slot * Geometry<D, MX>::kPageBytes);  // into the freed slot
+      if (j + NP < j1) request(nxt, ring_lds + slot * Geometry<D, MX>::kPageBytes);  // into the freed slot
       slot = slot + 1 == NP ? 0 : slot + 1;
     }
     tile_logits<MT>(acc1, ks1, wf, out, off1);  // the last tile
