@@ -224,16 +224,19 @@ idx_status check_queries(const uint16_t* q, const float* w, int heads) {
   return IDX_OK;
 }
 
-// Rows longer than the register path (kRowCap keys) in a batch of fewer
-// than kChunkRowsMax rows are split into chunks of kRowCap keys, each chunk
-// selected by its own workgroup, then merged per row (a pure function of
-// the rows and k, so that the workspace size does not depend on the device).
-constexpr int kChunkRowsMax = 512;
+// Rows longer than the register path (kRowCap keys) are split into chunks
+// of kRowCap keys, each chunk selected by its own workgroup, then merged per
+// row, when all the chunks fit one workgroup per CU of the target part
+// (kChunkWgMax); with more, a chunk's workgroup waits for a CU and one
+// workgroup per row streaming its row is faster.  (A pure function of the
+// rows and k, so that the workspace size does not depend on the device.)
+constexpr int kChunkWgMax = 256;
 
 int topk_chunks(const RowArgs& R) {
-  if (R.max_keys <= kRowCap || R.num_rows >= kChunkRowsMax) return 0;
+  if (R.max_keys <= kRowCap) return 0;
   const int64_t c = ceil_div(R.max_keys, kRowCap);
-  return c <= kMaxTopkChunks ? static_cast<int>(c) : 0;
+  if (c > kMaxTopkChunks || static_cast<int64_t>(R.num_rows) * c > kChunkWgMax) return 0;
+  return static_cast<int>(c);
 }
 
 // Workspace bytes of the chunk candidates (two [rows][chunks][k] arrays:

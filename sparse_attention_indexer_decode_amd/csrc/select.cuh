@@ -381,6 +381,243 @@ __device__ __forceinline__ void finish_candidates(int L, int k, const SelectStat
   __syncthreads();
 }
 
+// Linear bins over a value range [lo, hi]: bin(v) = clamp(fma(v, a, b), 0,
+// kD1Bins - 1) truncated, with a = kD1Bins / (hi - lo) and b = -lo a: one
+// rounding of (v - lo) a, so monotone non-decreasing in v.  (hi - lo is
+// formed from halves so that it cannot overflow; when a or b is not finite
+// every value goes to bin 0, which is slow but still exact.)
+struct LinearBins {
+  float a, b;
+  __device__ __forceinline__ static LinearBins over(float lo, float hi) {
+    const float half_range = hi * 0.5f - lo * 0.5f;
+    float a = half_range > 0.0f ? static_cast<float>(kD1Bins / 2) / half_range : 0.0f;
+    float b = -(lo * a);
+    if (!(__builtin_fabsf(a) <= 3.0e38f) || !(__builtin_fabsf(b) <= 3.0e38f)) a = b = 0.0f;
+    return {a, b};
+  }
+  __device__ __forceinline__ float raw(float v) const { return __builtin_fmaf(v, a, b); }
+  __device__ __forceinline__ int bin(float v) const {
+    return static_cast<int>(__builtin_amdgcn_fmed3f(raw(v), 0.0f, static_cast<float>(kD1Bins - 1)));
+  }
+};
+
+// The V float4 quads q = c NT + tid (c < V) of the chunk at `base` (V
+// loads in flight together; each load instruction of a wave covers 1 KiB of
+// consecutive keys); element j of the thread is position
+// base + 4 (j / 4 NT + tid) + j % 4, or -inf past the row's end.
+template <int V, int NT>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int base, int L, bool aligned,
+                                           float (&f)[4 * V]) {
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    const int i0 = base + 4 * (c * NT + static_cast<int>(threadIdx.x));
+    if (aligned && i0 + 4 <= L) {
+      const float4 x = *reinterpret_cast<const float4*>(row + i0);
+      f[4 * c] = x.x;
+      f[4 * c + 1] = x.y;
+      f[4 * c + 2] = x.z;
+      f[4 * c + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * c + j] = (i0 + j) < L ? row[i0 + j] : -__builtin_inff();
+    }
+  }
+}
+
+// Appends every key of the row that passes `test` (monotone in the value,
+// false for -inf) to the LDS candidate list as (float bits, position), at
+// most kCandCap of them; returns how many there are (also when more than
+// fit).  Per chunk, each wave counts its passing keys with ballots,
+// reserves that many slots at once and writes its keys at ballot offsets;
+// the loads of the next chunk are in flight while a chunk is tested.
+template <int NT, class Test>
+__device__ __forceinline__ int collect_by(const float* __restrict__ row, int L, bool aligned, Test test,
+                                          SelectShared<NT>& sm) {
+  if (threadIdx.x == 0) sm.bc[4] = 0;
+  __syncthreads();
+  constexpr int V = NT == 512 ? 4 : 8;
+  constexpr int kStep = NT * 4 * V;
+  const int lane = lane_id();
+  auto process = [&](const float (&f)[4 * V], int base) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4 * V; ++j) cnt += __popcll(__ballot(test(f[j])));
+    int wbase = 0;
+    if (lane == 0 && cnt > 0) wbase = atomicAdd(&sm.bc[4], cnt);
+    wbase = __builtin_amdgcn_readfirstlane(wbase);
+    if (wbase + cnt <= kCandCap) {  // (else the list is full: counted only)
+      const int pbase = base + 4 * static_cast<int>(threadIdx.x);
+#pragma unroll
+      for (int j = 0; j < 4 * V; ++j) {
+        const bool pj = test(f[j]);
+        const uint64_t m = __ballot(pj);
+        if (m) {
+          if (pj) {
+            const int off = wbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                        static_cast<uint32_t>(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+            sm.c.ckey[off] = __float_as_uint(f[j]);
+            sm.c.cidx[off] = pbase + 4 * NT * (j / 4) + (j % 4);
+          }
+          wbase += __popcll(m);
+        }
+      }
+    }
+  };
+  // two register buffers in turn: a chunk's loads are in flight while the
+  // chunk before it is tested
+  float fa[4 * V], fb[4 * V];
+  load_chunk<V, NT>(row, 0, L, aligned, fa);
+  for (int base = 0; base < L; base += 2 * kStep) {
+    if (base + kStep < L) load_chunk<V, NT>(row, base + kStep, L, aligned, fb);
+    process(fa, base);
+    if (base + kStep >= L) break;
+    if (base + 2 * kStep < L) load_chunk<V, NT>(row, base + 2 * kStep, L, aligned, fa);
+    process(fb, base + kStep);
+  }
+  __syncthreads();
+  return sm.bc[4];
+}
+
+// Exact top k of a row from its `nc` candidates in LDS (float bits and
+// positions; every key of the row's top k is among them, k <= nc <=
+// kCandCap): linear bins over the candidates' range give the bin B1 holding
+// the k-th largest; candidates above it win, and the `need` winners of bin
+// B1 are decided on the exact key (rank against each other when few, radix
+// passes otherwise), ties to the lower position.  Winners go to an LDS
+// position bitmap and one ordered scan writes the k positions.  Needs
+// L <= kBitmapWords * 32.
+template <int NT>
+__device__ __forceinline__ void select_candidates(int L, int k, int nc, int* __restrict__ out, SelectShared<NT>& sm) {
+  constexpr int CPT = kCandCap / NT;  // candidates per thread: i = tid + NT c
+  static_assert(kRankCap <= NT, "a rank verdict per thread");
+  const int tid = threadIdx.x;
+  float cv[CPT];
+  int cp[CPT];
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int i = tid + NT * c;
+    cv[c] = i < nc ? __uint_as_float(sm.c.ckey[i]) : 0.0f;
+    cp[c] = i < nc ? sm.c.cidx[i] : -1;
+    if (i < nc) {
+      lo = fminf(lo, cv[c]);
+      hi = fmaxf(hi, cv[c]);
+    }
+  }
+  __syncthreads();  // the list is in registers: its LDS is free
+  for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
+  block_min_max<NT>(lo, hi, sm.c.cidx);  // (its barrier also publishes the cleared bins)
+  const LinearBins lb = LinearBins::over(lo, hi);
+  int bn[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    bn[c] = cp[c] >= 0 ? lb.bin(cv[c]) : -1;
+    if (bn[c] >= 0) atomicAdd(&sm.u.hist1[bn[c]], 1);
+  }
+  __syncthreads();
+  if (tid == 0) sm.bc[4] = 0;  // eq-list counter, published by find_digit's barrier
+  int B1, above1, m;
+  find_digit<NT, false>(kD1Bins, k, [&](int d) { return sm.u.hist1[d]; }, sm, B1, above1, m);
+  const int need = k - above1;  // keys of bin B1 to take
+  // keys of bin B1 -> the front of the (free) candidate area, exact keys
+  uint32_t* eq_key = sm.c.ckey;
+  int* eq_pos = sm.c.cidx;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    if (bn[c] == B1) {
+      const int slot = atomicAdd(&sm.bc[4], 1);
+      eq_key[slot] = ordered_key(cv[c]);
+      eq_pos[slot] = cp[c];
+    }
+  }
+  __syncthreads();
+
+  // the `need` winners of bin B1, decided before the bitmap exists (the
+  // second-digit histogram may share its memory): all of them, a rank
+  // verdict per thread (few keys: entry tid), or a radix rule on (key,
+  // position)
+  const bool take_all = need == m;
+  bool rank_win = false;
+  SelectState st{0u, 0u, need};
+  SelectState ts{0u, 0u, 0};
+  bool rule_all_eq = true;
+  if (!take_all) {
+    if (m <= kRankCap) {
+      if (tid < m) {
+        const uint32_t ki = eq_key[tid];
+        const int pi = eq_pos[tid];
+        int rank = 0;
+        for (int u = 0; u < m; ++u) {
+          const uint32_t ku = eq_key[u];
+          rank += (ku > ki || (ku == ki && eq_pos[u] < pi)) ? 1 : 0;
+        }
+        rank_win = rank < need;
+      }
+    } else {
+      auto in_bin = [&](auto fn) {
+        for (int i = tid; i < m; i += NT) fn(eq_key[i]);
+      };
+      int n_eq = refine_pass<NT>(st, 21, 11, in_bin, sm);
+      if (st.need != n_eq) n_eq = refine_pass<NT>(st, 10, 11, in_bin, sm);
+      if (st.need != n_eq) n_eq = refine_pass<NT>(st, 0, 10, in_bin, sm);
+      rule_all_eq = st.need == n_eq;
+      if (!rule_all_eq) {
+        // keys equal to the threshold: the `need` lowest positions among
+        // them, i.e. the largest of (2^17 - 1 - position)
+        ts.need = st.need;
+        const uint32_t prefix = st.prefix, pmask = st.pmask;
+        refine<NT>(ts, 8, 9, 0, 8, [&](auto fn) {
+          for (int i = tid; i < m; i += NT)
+            if ((eq_key[i] & pmask) == prefix) fn(0x1FFFFu - static_cast<uint32_t>(eq_pos[i]));
+        }, sm);
+      }
+    }
+  }
+  const int W = (L + 31) >> 5;
+  uint32_t* bits = sm.u.sel;
+  __syncthreads();  // every histogram read is done: the bitmap may take the memory
+  for (int j = tid; j < W; j += NT) bits[j] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+    if (bn[c] > B1) atomicOr(&bits[cp[c] >> 5], 1u << (cp[c] & 31));
+  if (take_all) {
+    for (int i = tid; i < m; i += NT) atomicOr(&bits[eq_pos[i] >> 5], 1u << (eq_pos[i] & 31));
+  } else if (m <= kRankCap) {
+    if (rank_win) atomicOr(&bits[eq_pos[tid] >> 5], 1u << (eq_pos[tid] & 31));
+  } else {
+    const uint32_t prefix = st.prefix, pmask = st.pmask;
+    for (int i = tid; i < m; i += NT) {
+      const uint32_t mk = eq_key[i] & pmask;
+      const int pi = eq_pos[i];
+      const bool win = mk > prefix ||
+                       (mk == prefix && (rule_all_eq || (0x1FFFFu - static_cast<uint32_t>(pi)) >= ts.prefix));
+      if (win) atomicOr(&bits[pi >> 5], 1u << (pi & 31));
+    }
+  }
+  __syncthreads();
+
+  // ordered emission: thread t owns bitmap words [t wpt, (t + 1) wpt)
+  const int wpt = (W + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  const int w1 = (w0 + wpt < W) ? w0 + wpt : W;
+  int c_sel = 0;
+  for (int wd = w0; wd < w1; ++wd) c_sel += __popc(bits[wd]);
+  int tot;
+  int o = block_exclusive_scan<NT>(c_sel, tot, sm.scan);
+  for (int wd = w0; wd < w1; ++wd) {
+    uint32_t sel = bits[wd];
+    while (sel) {
+      const int bpos = __builtin_ctz(sel);
+      sel &= sel - 1u;
+      if (o < k) out[o] = wd * 32 + bpos;
+      ++o;
+    }
+  }
+  __syncthreads();
+}
+
 // Rows this long (and of at most kBitmapWords * 32 keys) with k at most
 // kSampleMaxK first try one read (the candidate window [k, kCandCap] around
 // the expected 1.5 k keeps a fallback rare):
@@ -388,14 +625,15 @@ constexpr int kSampleMinLen = 16384;
 constexpr int kSampleMaxK = 2048;
 
 // One-read selection of a streamed row: a systematic sample (every S-th
-// 64-key block, at most kCandCap keys) gives a key K0 that about 1.5 k of the
-// row's keys reach -- the sample's ceil(1.5 k / S)-th largest -- and one pass
-// collects every key >= K0.  When that holds at least k and at most
-// kCandCap keys, every key of the top k is among them (the top k are >= the
-// k-th largest >= K0, since at least k keys are >= K0) and the exact
-// selection runs on them; otherwise (a skewed sample, heavy ties) nothing is
-// written and the caller takes the two-read path.  Returns whether it
-// finished the row (the same on every thread).
+// 64-key block, at most kCandCap keys) in linear bins over its own range
+// gives the bin holding its ceil(1.5 k / S)-th largest value, i.e. a
+// threshold that about 1.5 k of the row's keys reach; one pass collects every
+// key at or above it (a test monotone in the value).  When that holds at
+// least k and at most kCandCap keys, every key of the top k is among them
+// (the top k are >= the k-th largest, which passes the test since at least k
+// keys do) and the exact selection runs on them; otherwise (a skewed sample,
+// heavy ties) nothing is written and the caller takes the two-read path.
+// Returns whether it finished the row (the same on every thread).
 template <int NT>
 __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row, int L, int k, bool aligned,
                                                    int* __restrict__ out, SelectShared<NT>& sm) {
@@ -407,6 +645,7 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   static_assert(64 * 64 <= kCandCap, "the sample must fit the candidate area");
   const int r = (3 * k + 2 * S - 1) / (2 * S);            // ceil(1.5 k / S)
   if (r < 1 || r > ns) return false;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
   for (int qi = tid; qi < ns_blocks * 16; qi += NT) {
     const int pos = (qi >> 4) * S * 64 + (qi & 15) * 4;
     float f0, f1, f2, f3;
@@ -416,34 +655,27 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
     } else {
       f0 = row[pos]; f1 = row[pos + 1]; f2 = row[pos + 2]; f3 = row[pos + 3];
     }
-    sm.c.ckey[4 * qi] = ordered_key(f0);
-    sm.c.ckey[4 * qi + 1] = ordered_key(f1);
-    sm.c.ckey[4 * qi + 2] = ordered_key(f2);
-    sm.c.ckey[4 * qi + 3] = ordered_key(f3);
+    sm.c.ckey[4 * qi] = __float_as_uint(f0);
+    sm.c.ckey[4 * qi + 1] = __float_as_uint(f1);
+    sm.c.ckey[4 * qi + 2] = __float_as_uint(f2);
+    sm.c.ckey[4 * qi + 3] = __float_as_uint(f3);
+    lo = fminf(fminf(lo, fminf(f0, f1)), fminf(f2, f3));
+    hi = fmaxf(fmaxf(hi, fmaxf(f0, f1)), fmaxf(f2, f3));
   }
+  for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
+  block_min_max<NT>(lo, hi, sm.c.cidx);  // (its barrier also publishes the sample and the cleared bins)
+  const LinearBins lb = LinearBins::over(lo, hi);
+  if (!(lb.a > 0.0f)) return false;  // one value, or an infinite range: the two-read path
+  for (int i = tid; i < ns; i += NT) atomicAdd(&sm.u.hist1[lb.bin(__uint_as_float(sm.c.ckey[i]))], 1);
   __syncthreads();
-  // the lower edge of the 22-bit digit bin holding the sample's r-th largest
-  // key (or of its 11-bit bin when that is taken whole): only lower, never
-  // higher, than the r-th largest
-  SelectState ss{0u, 0u, r};
-  auto in_sample = [&](auto fn) {
-    for (int i = tid; i < ns; i += NT) fn(sm.c.ckey[i]);
-  };
-  const int cnt = refine_pass<NT>(ss, 21, 11, in_sample, sm);
-  if (ss.need != cnt) refine_pass<NT>(ss, 10, 11, in_sample, sm);   // 22 bits: a bound, not the exact key
-  const uint32_t k0 = ss.prefix;
-  __syncthreads();  // the sample area is reused for the candidates
-
-  const int nc = collect_candidates<NT>(row, L, aligned, k0, sm);
+  int B0, above0, cnt0;
+  find_digit<NT>(kD1Bins, r, [&](int d) { return sm.u.hist1[d]; }, sm, B0, above0, cnt0);
+  // keys whose unclamped bin value reaches B0: monotone in the value, and
+  // every sample key of bin B0 and above passes
+  const float t0 = static_cast<float>(B0);
+  const int nc = collect_by<NT>(row, L, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm);
   if (nc < k || nc > kCandCap) return false;
-  SelectState st{0u, 0u, k};
-  auto in_cand = [&](auto fn) {
-    for (int i = tid; i < nc; i += NT) fn(sm.c.ckey[i]);
-  };
-  int n_eq = refine_pass<NT>(st, 21, 11, in_cand, sm);
-  if (st.need != n_eq) n_eq = refine_pass<NT>(st, 10, 11, in_cand, sm);
-  if (st.need != n_eq) n_eq = refine_pass<NT>(st, 0, 10, in_cand, sm);
-  finish_candidates<NT>(L, k, st, n_eq, nc, out, sm);
+  select_candidates<NT>(L, k, nc, out, sm);
   return true;
 }
 
