@@ -399,13 +399,16 @@ def run_decode(wl, args, pools=None) -> dict:
     step_ms = wall_ms(lambda i: step(args.warmup + i), args.steps)
     assert torch.equal(first, outs), f"{wl.name}: decode top-k is not deterministic across steps"
 
-    # the same steps replayed from a HIP graph (one graph holds one step per pool copy)
-    g = capture(step, copies)
-    reps = max(1, args.steps // copies)
+    # the same steps replayed from a HIP graph: one graph holds at least
+    # eight steps (cycling the pool copies), so that a replay's own launch
+    # cost is spread as it would be in a serving loop
+    n_graph = max(copies, 8)
+    g = capture(step, n_graph)
+    reps = max(1, args.steps // n_graph)
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(first, outs), f"{wl.name}: graph replay differs from eager"
-    graph_ms = wall_ms(lambda i: g.replay(), reps) / copies
+    graph_ms = wall_ms(lambda i: g.replay(), reps) / n_graph
     assert torch.equal(first, outs), f"{wl.name}: graph replay differs from eager"
 
     # per-kernel launch durations: HIP events around back-to-back launches
