@@ -189,6 +189,15 @@ def test_workspace_sizes(lib):
     # many rows take the one-workgroup-per-row streaming path: no candidates
     rm = _rows(num_req=600, max_seq_len=131072, bt_width=2048)
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rm), 0, 2048) == 256
+    # rows are split only while all their chunks fit 256 workgroups: 64 rows of
+    # four 32768-key chunks are split, 65 are not, nor are 128 MTP rows
+    # (64 requests x next_n 2) of four chunks; 128 rows of two chunks are
+    r65 = _rows(num_req=65, max_seq_len=131072, bt_width=2048, bt_stride=2048)
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r65), 0, 2048) == 256
+    r64x2 = _rows(num_req=64, next_n=2, max_seq_len=131072, bt_width=2048, bt_stride=2048)
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r64x2), 0, 2048) == 256
+    r128 = _rows(num_req=128, max_seq_len=65536, bt_width=1024, bt_stride=1024)
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r128), 0, 2048) == 256 + 2 * 4 * 128 * 2 * 2048
     assert lib.idx_num_rows(ctypes.byref(_rows(num_req=3, next_n=2))) == 6
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=9))) == 5
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=3))) == -1
