@@ -24,7 +24,14 @@
 //      list, radix passes on the 32-bit key and then on positions otherwise)
 //      and added to the bitmap;
 //   5. one ordered scan over the bitmap writes the k positions.
-// Longer rows stream from global memory:
+// Longer rows stream from global memory.  Rows of 16384..131072 keys with
+// k <= 2048 first try one read (select_row_sampled): a systematic sample in
+// linear bins over its own range gives a threshold that about 1.5 k keys
+// reach, one pass collects the keys at or above it (ballot-compacted into
+// LDS), and when at least k and at most kCandCap were collected the exact
+// selection runs on them (select_candidates: linear bins over their range,
+// the threshold bin's keys ranked or radix-selected, the bitmap, the ordered
+// scan).  Otherwise, and for other rows:
 //   1. d1 histogram of the row in LDS, one pass with many coalesced loads in
 //      flight.
 //   2. The d1 bin B1 holding the k-th largest; every element with d1 >= B1
