@@ -89,13 +89,76 @@ struct SelectState {
   int need;  // elements equal (under pmask) to prefix still to take
 };
 
-// Loads keys [i0, i0 + 4*V) of a row into registers (vector loads when the
-// row is 16-byte aligned), so that all V loads are in flight together.
+// Streaming loads.  No load may sit under a lane-dependent branch: both
+// sides of such a branch run, they share registers, and the compiler then
+// waits for every earlier load before each one -- one memory round trip per
+// load instead of all of them in flight together.  The form is chosen by
+// conditions that are the same on every lane.
+
+// The keys base + 4 (c NT + tid) + e (c < V, e < 4) of a row of L >= 1
+// keys, keys past L read as `pad`.  A 16-byte aligned row is read in 16-byte
+// quads at clamped quad positions (the 1..3 keys after the row's last whole
+// quad come from three loads every lane makes alike); an unaligned row key
+// by key, one quad's four loads at a time.
+template <int V, int NT>
+__device__ __forceinline__ void load_quads(const float* __restrict__ row, int base, int L, bool aligned, float pad,
+                                           float (&f)[4 * V]) {
+  const int tid = threadIdx.x;
+  if (aligned && base + 4 * V * NT <= L) {  // every quad whole
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(row + base + 4 * (c * NT + tid));
+      f[4 * c] = x.x;
+      f[4 * c + 1] = x.y;
+      f[4 * c + 2] = x.z;
+      f[4 * c + 3] = x.w;
+    }
+  } else if (aligned && L >= 4) {
+    const int Lq = L & ~3;  // keys [0, Lq) form whole quads
+    const float t0 = row[Lq < L ? Lq : L - 1];
+    const float t1 = row[Lq + 1 < L ? Lq + 1 : L - 1];
+    const float t2 = row[Lq + 2 < L ? Lq + 2 : L - 1];
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      const int i0 = base + 4 * (c * NT + tid);  // a multiple of 4, as is Lq
+      const float4 x = *reinterpret_cast<const float4*>(row + (i0 + 4 <= Lq ? i0 : Lq - 4));
+      const float xe[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const int d = i - Lq;
+        const float tail = d == 0 ? t0 : (d == 1 ? t1 : t2);
+        f[4 * c + e] = i < Lq ? xe[e] : (i < L ? tail : pad);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = base + 4 * (c * NT + tid) + e;
+        const float x = row[i < L ? i : L - 1];
+        f[4 * c + e] = i < L ? x : pad;
+      }
+      // this quad's loads complete before the next quad's are issued, so
+      // that the unrolled loads do not all hold address registers at once
+      __asm__ volatile("" : "+v"(f[4 * c]), "+v"(f[4 * c + 1]), "+v"(f[4 * c + 2]), "+v"(f[4 * c + 3]));
+    }
+  }
+}
+
+// Loads in the form of load_quads, for contiguous per-lane keys: `whole`
+// (the same on every lane) says every lane's keys lie in the row and the
+// row is 16-byte aligned; otherwise each key is loaded from a clamped
+// position (L >= 1), one quad at a time, and the keys past L are flagged.
+
+// Loads keys [i0, i0 + 4*V) of a row into registers, all V loads in flight
+// together.
 template <int V>
-__device__ __forceinline__ void load_keys(const float* __restrict__ row, int i0, int L, bool aligned,
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int i0, int L, bool whole,
                                           uint32_t (&u)[4 * V], bool (&v)[4 * V]) {
   float f[4 * V];
-  if (aligned && i0 + 4 * V <= L) {
+  if (whole) {
 #pragma unroll
     for (int c = 0; c < V; ++c) {
       const float4 x = *reinterpret_cast<const float4*>(row + i0 + 4 * c);
@@ -108,9 +171,15 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int i0,
     for (int j = 0; j < 4 * V; ++j) v[j] = true;
   } else {
 #pragma unroll
-    for (int j = 0; j < 4 * V; ++j) {
-      v[j] = (i0 + j) < L;
-      f[j] = v[j] ? row[i0 + j] : 0.0f;
+    for (int c = 0; c < V; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 4 * c + e;
+        v[4 * c + e] = i < L;
+        const float x = row[i < L ? i : L - 1];
+        f[4 * c + e] = i < L ? x : 0.0f;
+      }
+      __asm__ volatile("" : "+v"(f[4 * c]), "+v"(f[4 * c + 1]), "+v"(f[4 * c + 2]), "+v"(f[4 * c + 3]));
     }
   }
 #pragma unroll
@@ -126,27 +195,12 @@ __device__ __forceinline__ void load_keys_strided(const float* __restrict__ row,
                                                   uint32_t (&u)[4 * V], bool (&v)[4 * V]) {
   const int tid = threadIdx.x;
   float f[4 * V];
+  load_quads<V, NT>(row, base, L, aligned, 0.0f, f);
 #pragma unroll
-  for (int c = 0; c < V; ++c) {
-    const int i0 = base + 4 * (c * NT + tid);
-    if (aligned && i0 + 4 <= L) {
-      const float4 x = *reinterpret_cast<const float4*>(row + i0);
-      f[4 * c] = x.x;
-      f[4 * c + 1] = x.y;
-      f[4 * c + 2] = x.z;
-      f[4 * c + 3] = x.w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * c + j] = true;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[4 * c + j] = (i0 + j) < L;
-        f[4 * c + j] = v[4 * c + j] ? row[i0 + j] : 0.0f;
-      }
-    }
+  for (int j = 0; j < 4 * V; ++j) {
+    v[j] = base + 4 * ((j / 4) * NT + tid) + (j % 4) < L;
+    u[j] = ordered_key(f[j]);
   }
-#pragma unroll
-  for (int j = 0; j < 4 * V; ++j) u[j] = ordered_key(f[j]);
 }
 
 template <int NT>
@@ -262,7 +316,7 @@ __device__ __forceinline__ void compact_global(const float* __restrict__ row, in
     const int i0 = base + tid * 4 * V;
     uint32_t u[4 * V];
     bool v[4 * V];
-    load_keys<V>(row, i0, L, aligned, u, v);
+    load_keys<V>(row, i0, L, aligned && base + NT * 4 * V <= L, u, v);
     bool gt[4 * V], eq[4 * V];
     int c_eq = 0;
 #pragma unroll
@@ -415,20 +469,7 @@ struct LinearBins {
 template <int V, int NT>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int base, int L, bool aligned,
                                            float (&f)[4 * V]) {
-#pragma unroll
-  for (int c = 0; c < V; ++c) {
-    const int i0 = base + 4 * (c * NT + static_cast<int>(threadIdx.x));
-    if (aligned && i0 + 4 <= L) {
-      const float4 x = *reinterpret_cast<const float4*>(row + i0);
-      f[4 * c] = x.x;
-      f[4 * c + 1] = x.y;
-      f[4 * c + 2] = x.z;
-      f[4 * c + 3] = x.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f[4 * c + j] = (i0 + j) < L ? row[i0 + j] : -__builtin_inff();
-    }
-  }
+  load_quads<V, NT>(row, base, L, aligned, -__builtin_inff(), f);
 }
 
 // Appends every key of the row that passes `test` (monotone in the value,
@@ -436,19 +477,31 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int ba
 // most kCandCap of them; returns how many there are (also when more than
 // fit).  Per chunk, each wave counts its passing keys with ballots,
 // reserves that many slots at once and writes its keys at ballot offsets;
-// the loads of the next chunk are in flight while a chunk is tested.
+// the loads of the next chunk are in flight while a chunk is tested.  The
+// caller has requested the first two chunks (collect_chunk_keys of them,
+// load_chunk) into fa and fb.
+template <int NT>
+constexpr int collect_chunk_keys() { return NT == 512 ? 16 : 32; }
+
 template <int NT, class Test>
 __device__ __forceinline__ int collect_by(const float* __restrict__ row, int L, bool aligned, Test test,
-                                          SelectShared<NT>& sm) {
+                                          SelectShared<NT>& sm, float (&fa)[collect_chunk_keys<NT>()],
+                                          float (&fb)[collect_chunk_keys<NT>()]) {
   if (threadIdx.x == 0) sm.bc[4] = 0;
   __syncthreads();
-  constexpr int V = NT == 512 ? 4 : 8;
+  constexpr int V = collect_chunk_keys<NT>() / 4;
   constexpr int kStep = NT * 4 * V;
   const int lane = lane_id();
   auto process = [&](const float (&f)[4 * V], int base) {
+    // one ballot per key slot; the writes below take their lanes from the
+    // same masks (as exec), not from a second evaluation of the test
+    uint64_t mk[4 * V];
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 4 * V; ++j) cnt += __popcll(__ballot(test(f[j])));
+    for (int j = 0; j < 4 * V; ++j) {
+      mk[j] = __ballot(test(f[j]));
+      cnt += __popcll(mk[j]);
+    }
     int wbase = 0;
     if (lane == 0 && cnt > 0) wbase = atomicAdd(&sm.bc[4], cnt);
     wbase = __builtin_amdgcn_readfirstlane(wbase);
@@ -456,10 +509,9 @@ __device__ __forceinline__ int collect_by(const float* __restrict__ row, int L, 
       const int pbase = base + 4 * static_cast<int>(threadIdx.x);
 #pragma unroll
       for (int j = 0; j < 4 * V; ++j) {
-        const bool pj = test(f[j]);
-        const uint64_t m = __ballot(pj);
+        const uint64_t m = mk[j];
         if (m) {
-          if (pj) {
+          if (__builtin_amdgcn_inverse_ballot_w64(m)) {
             const int off = wbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                                         static_cast<uint32_t>(m >> 32),
                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
@@ -473,14 +525,12 @@ __device__ __forceinline__ int collect_by(const float* __restrict__ row, int L, 
   };
   // two register buffers in turn: a chunk's loads are in flight while the
   // chunk before it is tested
-  float fa[4 * V], fb[4 * V];
-  load_chunk<V, NT>(row, 0, L, aligned, fa);
   for (int base = 0; base < L; base += 2 * kStep) {
-    if (base + kStep < L) load_chunk<V, NT>(row, base + kStep, L, aligned, fb);
     process(fa, base);
     if (base + kStep >= L) break;
     if (base + 2 * kStep < L) load_chunk<V, NT>(row, base + 2 * kStep, L, aligned, fa);
     process(fb, base + kStep);
+    if (base + 3 * kStep < L) load_chunk<V, NT>(row, base + 3 * kStep, L, aligned, fb);
   }
   __syncthreads();
   return sm.bc[4];
@@ -652,22 +702,42 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   static_assert(64 * 64 <= kCandCap, "the sample must fit the candidate area");
   const int r = (3 * k + 2 * S - 1) / (2 * S);            // ceil(1.5 k / S)
   if (r < 1 || r > ns) return false;
-  float lo = __builtin_inff(), hi = -__builtin_inff();
-  for (int qi = tid; qi < ns_blocks * 16; qi += NT) {
+  // the sample's quads (at most kCandCap / 4 of them, CQ per thread) are
+  // requested first and the collection's first two chunks right after, so
+  // that those are in flight while the sample is binned
+  constexpr int CQ = (kCandCap / 4 + NT - 1) / NT;
+  float sv[CQ][4];
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) {
+    // lanes past the sample load its last quad again (unused), so that no
+    // load sits under a lane-dependent branch
+    const int qi = tid + NT * c < ns_blocks * 16 ? tid + NT * c : ns_blocks * 16 - 1;
     const int pos = (qi >> 4) * S * 64 + (qi & 15) * 4;
-    float f0, f1, f2, f3;
     if (aligned) {
       const float4 x = *reinterpret_cast<const float4*>(row + pos);
-      f0 = x.x; f1 = x.y; f2 = x.z; f3 = x.w;
+      sv[c][0] = x.x; sv[c][1] = x.y; sv[c][2] = x.z; sv[c][3] = x.w;
     } else {
-      f0 = row[pos]; f1 = row[pos + 1]; f2 = row[pos + 2]; f3 = row[pos + 3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[c][e] = row[pos + e];
     }
-    sm.c.ckey[4 * qi] = __float_as_uint(f0);
-    sm.c.ckey[4 * qi + 1] = __float_as_uint(f1);
-    sm.c.ckey[4 * qi + 2] = __float_as_uint(f2);
-    sm.c.ckey[4 * qi + 3] = __float_as_uint(f3);
-    lo = fminf(fminf(lo, fminf(f0, f1)), fminf(f2, f3));
-    hi = fmaxf(fmaxf(hi, fmaxf(f0, f1)), fmaxf(f2, f3));
+  }
+  constexpr int V = collect_chunk_keys<NT>() / 4;
+  constexpr int kStep = NT * 4 * V;
+  float fa[4 * V], fb[4 * V];
+  load_chunk<V, NT>(row, 0, L, aligned, fa);
+  if (kStep < L) load_chunk<V, NT>(row, kStep, L, aligned, fb);
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < CQ; ++c) {
+    const int qi = tid + NT * c;
+    if (qi < ns_blocks * 16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.c.ckey[4 * qi + e] = __float_as_uint(sv[c][e]);
+        lo = fminf(lo, sv[c][e]);
+        hi = fmaxf(hi, sv[c][e]);
+      }
+    }
   }
   for (int j = tid; j < kD1Bins; j += NT) sm.u.hist1[j] = 0;
   block_min_max<NT>(lo, hi, sm.c.cidx);  // (its barrier also publishes the sample and the cleared bins)
@@ -680,7 +750,7 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   // keys whose unclamped bin value reaches B0: monotone in the value, and
   // every sample key of bin B0 and above passes
   const float t0 = static_cast<float>(B0);
-  const int nc = collect_by<NT>(row, L, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm);
+  const int nc = collect_by<NT>(row, L, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm, fa, fb);
   if (nc < k || nc > kCandCap) return false;
   select_candidates<NT>(L, k, nc, out, sm);
   return true;

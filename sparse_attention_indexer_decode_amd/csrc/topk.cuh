@@ -65,7 +65,7 @@ __device__ __forceinline__ void row_window(const RowArgs& R, int r, int& L_out, 
 
 // kReg: see select_row.
 template <int NT, bool kReg = true>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kReg ? 1 : 6))) void topk_kernel(TopkParams p) {
   __shared__ SelectShared<NT> sm;
   __shared__ int info[2];
   const int r = blockIdx.x;
