@@ -478,8 +478,8 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int ba
 // fit).  Per chunk, each wave counts its passing keys with ballots,
 // reserves that many slots at once and writes its keys at ballot offsets;
 // the loads of the next chunk are in flight while a chunk is tested.  The
-// caller has requested the first two chunks (collect_chunk_keys of them,
-// load_chunk) into fa and fb.
+// caller has requested the first two chunks (collect_chunk_keys keys per
+// lane each, load_chunk) into fa and fb.
 template <int NT>
 constexpr int collect_chunk_keys() { return NT == 512 ? 16 : 32; }
 
@@ -703,8 +703,9 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   const int r = (3 * k + 2 * S - 1) / (2 * S);            // ceil(1.5 k / S)
   if (r < 1 || r > ns) return false;
   // the sample's quads (at most kCandCap / 4 of them, CQ per thread) are
-  // requested first and the collection's first two chunks right after, so
-  // that those are in flight while the sample is binned
+  // requested first and the collection's first chunk right after, so that
+  // it is in flight while the sample is binned (its second chunk, requested
+  // here too, measured no better)
   constexpr int CQ = (kCandCap / 4 + NT - 1) / NT;
   float sv[CQ][4];
 #pragma unroll
@@ -725,7 +726,6 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   constexpr int kStep = NT * 4 * V;
   float fa[4 * V], fb[4 * V];
   load_chunk<V, NT>(row, 0, L, aligned, fa);
-  if (kStep < L) load_chunk<V, NT>(row, kStep, L, aligned, fb);
   float lo = __builtin_inff(), hi = -__builtin_inff();
 #pragma unroll
   for (int c = 0; c < CQ; ++c) {
@@ -750,6 +750,7 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   // keys whose unclamped bin value reaches B0: monotone in the value, and
   // every sample key of bin B0 and above passes
   const float t0 = static_cast<float>(B0);
+  if (kStep < L) load_chunk<V, NT>(row, kStep, L, aligned, fb);
   const int nc = collect_by<NT>(row, L, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm, fa, fb);
   if (nc < k || nc > kCandCap) return false;
   select_candidates<NT>(L, k, nc, out, sm);
