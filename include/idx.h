@@ -231,9 +231,11 @@ idx_status idx_logits_paged(const idx_cache* cache, const idx_rows* rows, const 
  *   k      1..4096
  *   out    device int32 [rows, k]
  * Workspace: idx_workspace_bytes(IDX_OP_TOPK, NULL, rows, 0, k) -- the
- * status word, plus the chunk candidates (2 x rows x ceil(max keys / 32768)
- * x k 4-byte values) when rows longer than 32768 keys are split over workgroups
- * (at most 131072 keys per row, and rows x chunks at most 256).
+ * status word, plus the chunk candidates when rows longer than 32768 keys are
+ * split over workgroups (at most 131072 keys per row, and rows x chunks at
+ * most 256, chunks = ceil(max keys / 32768)): 2 x rows x chunks x 4096 4-byte
+ * values and rows x chunks counts for k <= 2048, 2 x rows x chunks x k 4-byte
+ * values above.
  */
 idx_status idx_topk(const float* logits, int64_t logits_stride, const idx_rows* rows, int32_t k,
                     int32_t* out, void* workspace, size_t workspace_bytes, void* stream);

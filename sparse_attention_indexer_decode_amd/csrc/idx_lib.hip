@@ -239,11 +239,21 @@ int topk_chunks(const RowArgs& R) {
   return static_cast<int>(c);
 }
 
-// Workspace bytes of the chunk candidates (two [rows][chunks][k] arrays:
-// logits and row positions).
+// Long rows are split with one shared threshold when k allows the one-read
+// selection (topk_split_*: kCandCap candidates per chunk slot and a count
+// per slot), otherwise by a top-k per chunk (topk_chunk_kernel /
+// topk_merge_kernel: k per slot, contiguous per row).
+bool topk_split_sampled(int k) { return k <= kSampleMaxK; }
+
+// Workspace bytes of the chunk candidates (two [rows][chunks][cap] arrays,
+// logits and row positions, then the [rows][chunks] counts when sampled).
 size_t topk_chunk_bytes(const RowArgs& R, int k) {
   const int c = topk_chunks(R);
-  return c ? align_up(2 * sizeof(int32_t) * static_cast<size_t>(R.num_rows) * c * k, 256) : 0;
+  if (!c) return 0;
+  const size_t slots = static_cast<size_t>(R.num_rows) * c;
+  const bool sampled = topk_split_sampled(k);
+  const size_t cap = sampled ? kCandCap : static_cast<size_t>(k);
+  return align_up(2 * sizeof(int32_t) * slots * cap + (sampled ? sizeof(int32_t) * slots : 0), 256);
 }
 
 idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, int k, int32_t* out,
@@ -256,17 +266,29 @@ idx_status launch_topk(const float* logits, int64_t stride, const RowArgs& R, in
   p.out = out;
   const int nc = topk_chunks(R);
   if (nc > 0) {
-    const size_t n = static_cast<size_t>(R.num_rows) * nc * k;
+    const bool sampled = topk_split_sampled(k);
     p.chunks = nc;
+    p.cap = sampled ? kCandCap : k;
+    const size_t n = static_cast<size_t>(R.num_rows) * nc * p.cap;
     p.cand_val = static_cast<float*>(chunk_ws);
     p.cand_pos = reinterpret_cast<int32_t*>(p.cand_val + n);
-    // dynamic LDS: the k selected positions of a chunk or a merge, sized so
-    // that two of these workgroups never share a CU (the launch has at most
-    // a few hundred; doubling up would halve their speed)
+    p.cand_cnt = p.cand_pos + n;
+    // dynamic LDS: the k selected positions of a chunk or a merge
+    // (topk_chunk_kernel, topk_merge_kernel; the split kernels leave it
+    // unused), sized so that two of these workgroups never share a CU (the
+    // launch has at most a few hundred; doubling up would halve their speed)
     constexpr unsigned kOneWgPerCu = 48 * 1024;
     static_assert(kOneWgPerCu >= sizeof(int32_t) * kMaxK, "k positions must fit the dynamic LDS");
-    hipLaunchKernelGGL(topk_chunk_kernel<kTopkThreads>, dim3(R.num_rows * nc), dim3(kTopkThreads), kOneWgPerCu, s, p);
-    hipLaunchKernelGGL(topk_merge_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), kOneWgPerCu, s, p);
+    if (sampled) {
+      hipLaunchKernelGGL(topk_split_collect_kernel<kTopkThreads>, dim3(R.num_rows * nc), dim3(kTopkThreads),
+                         kOneWgPerCu, s, p);
+      hipLaunchKernelGGL(topk_split_merge_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), kOneWgPerCu,
+                         s, p);
+    } else {
+      hipLaunchKernelGGL(topk_chunk_kernel<kTopkThreads>, dim3(R.num_rows * nc), dim3(kTopkThreads), kOneWgPerCu, s,
+                         p);
+      hipLaunchKernelGGL(topk_merge_kernel<kTopkThreads>, dim3(R.num_rows), dim3(kTopkThreads), kOneWgPerCu, s, p);
+    }
     return hipGetLastError() == hipSuccess ? IDX_OK : fail(IDX_EHIP, "kernel launch failed");
   }
   // Batches whose rows may exceed the register path and that have at least

@@ -691,9 +691,18 @@ constexpr int kSampleMaxK = 2048;
 // keys do) and the exact selection runs on them; otherwise (a skewed sample,
 // heavy ties) nothing is written and the caller takes the two-read path.
 // Returns whether it finished the row (the same on every thread).
+//
+// sample_threshold is its first part: the sample, its bins and the bin B0;
+// the keys to collect are those with lb.raw(v) >= t0.  It also requests
+// the first collection chunk of the keys (crow, cL) into fa, after the
+// sample's own loads.  Returns false (the same on every thread) when the
+// sample gives no threshold.  Its result depends on the row only, so
+// workgroups that collect different parts of one row agree on it.
 template <int NT>
-__device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row, int L, int k, bool aligned,
-                                                   int* __restrict__ out, SelectShared<NT>& sm) {
+__device__ __forceinline__ bool sample_threshold(const float* __restrict__ row, int L, int k, bool aligned,
+                                                 const float* __restrict__ crow, int cL,
+                                                 float (&fa)[collect_chunk_keys<NT>()], SelectShared<NT>& sm,
+                                                 LinearBins& lb_out, float& t0_out) {
   const int tid = threadIdx.x;
   const int nb = L >> 6;                                  // full 64-key blocks
   const int S = (nb + 63) / 64 > 16 ? (nb + 63) / 64 : 16;   // stride: >= 16, and <= 64 sampled blocks
@@ -723,9 +732,7 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
     }
   }
   constexpr int V = collect_chunk_keys<NT>() / 4;
-  constexpr int kStep = NT * 4 * V;
-  float fa[4 * V], fb[4 * V];
-  load_chunk<V, NT>(row, 0, L, aligned, fa);
+  load_chunk<V, NT>(crow, 0, cL, aligned, fa);
   float lo = __builtin_inff(), hi = -__builtin_inff();
 #pragma unroll
   for (int c = 0; c < CQ; ++c) {
@@ -749,7 +756,20 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   find_digit<NT>(kD1Bins, r, [&](int d) { return sm.u.hist1[d]; }, sm, B0, above0, cnt0);
   // keys whose unclamped bin value reaches B0: monotone in the value, and
   // every sample key of bin B0 and above passes
-  const float t0 = static_cast<float>(B0);
+  lb_out = lb;
+  t0_out = static_cast<float>(B0);
+  return true;
+}
+
+template <int NT>
+__device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row, int L, int k, bool aligned,
+                                                   int* __restrict__ out, SelectShared<NT>& sm) {
+  constexpr int V = collect_chunk_keys<NT>() / 4;
+  constexpr int kStep = NT * 4 * V;
+  float fa[4 * V], fb[4 * V];
+  LinearBins lb;
+  float t0;
+  if (!sample_threshold<NT>(row, L, k, aligned, row, L, fa, sm, lb, t0)) return false;
   if (kStep < L) load_chunk<V, NT>(row, kStep, L, aligned, fb);
   const int nc = collect_by<NT>(row, L, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm, fa, fb);
   if (nc < k || nc > kCandCap) return false;
@@ -757,12 +777,13 @@ __device__ __forceinline__ bool select_row_sampled(const float* __restrict__ row
   return true;
 }
 
-// Top-k of a row streamed from global memory (k < L).
+// Top-k of a row streamed from global memory (k < L); try_sampled = false
+// skips the one-read attempt (known to fail).
 template <int NT>
 __device__ __forceinline__ void select_row_stream(const float* __restrict__ row, int L, int k, int* __restrict__ out,
-                                  SelectShared<NT>& sm) {
+                                  SelectShared<NT>& sm, bool try_sampled = true) {
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  if (L >= kSampleMinLen && L <= kBitmapWords * 32 && k <= kSampleMaxK &&
+  if (try_sampled && L >= kSampleMinLen && L <= kBitmapWords * 32 && k <= kSampleMaxK &&
       select_row_sampled<NT>(row, L, k, aligned, out, sm))
     return;
 

@@ -12,10 +12,13 @@ struct TopkParams {
   RowArgs rows;
   int32_t k;
   int32_t* out;
-  // long rows split over workgroups (topk_chunk_kernel / topk_merge_kernel)
+  // long rows split over workgroups (topk_chunk_kernel / topk_merge_kernel,
+  // or topk_split_collect_kernel / topk_split_merge_kernel)
   int32_t chunks;     // chunk slots per row (ceil(max_keys / kRowCap))
-  float* cand_val;    // [rows][chunks * k] candidate logits in position order
-  int32_t* cand_pos;  // [rows][chunks * k] their positions in the row
+  int32_t cap;        // candidates per chunk slot
+  float* cand_val;    // [rows][chunks][cap] candidate logits
+  int32_t* cand_pos;  // [rows][chunks][cap] their positions in the row
+  int32_t* cand_cnt;  // [rows][chunks] candidates per chunk, -1: none usable (split collect only)
 };
 
 // Key count L and logits column base of row r (DECODE grid row or PREFILL
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkParams p) {
   const int lo = c * kRowCap;
   if (lo >= L) return;
   const int Lc = L - lo < kRowCap ? L - lo : kRowCap;
-  const int64_t slot = (static_cast<int64_t>(r) * p.chunks + c) * p.k;
+  const int64_t slot = (static_cast<int64_t>(r) * p.chunks + c) * p.cap;
   // the chunk's k selected positions go to the launch's dynamic LDS
   extern __shared__ int sel_pos[];
   select_row<NT>(row + lo, Lc, p.k, sel_pos, sm);
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   // every chunk but the last has more than k keys (kRowCap > k): its k
   // entries are all positions; the last has min(last, k)
   const int n = (nc - 1) * k + (last < k ? last : k);
-  const int64_t base = static_cast<int64_t>(r) * p.chunks * k;
+  const int64_t base = static_cast<int64_t>(r) * p.chunks * p.cap;  // (cap = k here)
   const float* val = p.cand_val + base;
   const int32_t* pos = p.cand_pos + base;
   int32_t* out = p.out + static_cast<int64_t>(r) * k;
@@ -150,6 +153,119 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkParams p) {
   else select_row_reg<NT, kRowCap / NT>(val, n, k, sel_idx, sm);
   __syncthreads();
   for (int j = threadIdx.x; j < k; j += NT) out[j] = pos[sel_idx[j]];
+}
+
+// Long rows split over workgroups with one threshold (k <= kSampleMaxK):
+// the one-read selection of select_row_sampled cut at its collection.
+// Every workgroup of a long row bins the same sample of the whole row
+// (sample_threshold), so all of them hold the same threshold, and each
+// collects the keys of its kRowCap-key chunk at or above it -- together
+// exactly the row's keys at or above it -- into its slot of the candidate
+// arrays, with their row positions and their count (-1 when the sample
+// gave no threshold or the chunk holds more than kCandCap).  A row of at
+// most kRowCap keys is finished by its chunk 0.  Then one workgroup per long
+// row (topk_split_merge_kernel) gathers the chunks' candidates and, when
+// they number at least k and at most kCandCap, selects exactly among them
+// (select_candidates: the row's top k are among the keys at or above a
+// value that at least k keys reach); otherwise it selects from the whole row
+// by the two-read path.  Workgroup numbering as in topk_chunk_kernel.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_split_collect_kernel(TopkParams p) {
+  static_assert(kRowCap <= NT * collect_chunk_keys<NT>(), "a chunk is one collection step");
+  __shared__ SelectShared<NT> sm;
+  __shared__ int info[2];
+  const int nr = gridDim.x / p.chunks;
+  const int c = blockIdx.x / nr;
+  const int r = blockIdx.x - c * nr;
+  int L, col0;
+  row_window<NT>(p.rows, r, L, col0, sm.scan, info);
+  const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
+  if (L <= kRowCap) {
+    if (c == 0) select_row<NT>(row, L, p.k, p.out + static_cast<int64_t>(r) * p.k, sm);
+    return;
+  }
+  const int lo = c * kRowCap;
+  if (lo >= L) return;
+  const int Lc = L - lo < kRowCap ? L - lo : kRowCap;
+  const int64_t slot = static_cast<int64_t>(r) * p.chunks + c;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;  // (lo keeps the alignment)
+  float fa[collect_chunk_keys<NT>()], fb[collect_chunk_keys<NT>()];
+  LinearBins lb;
+  float t0;
+  int n = -1;
+  if (L <= kBitmapWords * 32 && sample_threshold<NT>(row, L, p.k, aligned, row + lo, Lc, fa, sm, lb, t0)) {
+    n = collect_by<NT>(row + lo, Lc, aligned, [&](float v) { return lb.raw(v) >= t0; }, sm, fa, fb);
+    if (n > kCandCap) n = -1;
+  }
+  if (n > 0) {
+    float* val = p.cand_val + slot * p.cap;
+    int32_t* pos = p.cand_pos + slot * p.cap;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      val[i] = __uint_as_float(sm.c.ckey[i]);
+      pos[i] = lo + sm.c.cidx[i];
+    }
+  }
+  if (threadIdx.x == 0) p.cand_cnt[slot] = n;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_split_merge_kernel(TopkParams p) {
+  __shared__ SelectShared<NT> sm;
+  __shared__ int info[2];
+  __shared__ int cnt[kMaxTopkChunks];
+  const int r = blockIdx.x;
+  int L, col0;
+  row_window<NT>(p.rows, r, L, col0, sm.scan, info);
+  if (L <= kRowCap) return;  // finished by its chunk
+  const int k = p.k;
+  const int nc = (L + kRowCap - 1) / kRowCap;
+  const int64_t slot0 = static_cast<int64_t>(r) * p.chunks;
+  if (static_cast<int>(threadIdx.x) < nc) cnt[threadIdx.x] = p.cand_cnt[slot0 + threadIdx.x];
+  __syncthreads();
+  int total = 0;
+  bool ok = true;
+  for (int c = 0; c < nc; ++c) {
+    ok = ok && cnt[c] >= 0;
+    total += cnt[c] > 0 ? cnt[c] : 0;
+  }
+  const float* row = p.logits + static_cast<int64_t>(r) * p.stride + col0;
+  int32_t* out = p.out + static_cast<int64_t>(r) * k;
+  if (!ok || total < k || total > kCandCap) {
+    select_row_stream<NT>(row, L, k, out, sm, false);
+    return;
+  }
+  // the chunks' candidates, one after another, into the candidate area;
+  // every lane's loads in flight together (lanes past a chunk's count load
+  // its last candidate again and store nothing)
+  int off = 0;
+  for (int c = 0; c < nc; ++c) {
+    const int n = cnt[c];
+    if (n > 0) {
+      const float* val = p.cand_val + (slot0 + c) * p.cap;
+      const int32_t* pos = p.cand_pos + (slot0 + c) * p.cap;
+      constexpr int S = (kCandCap + NT - 1) / NT;
+      float v[S];
+      int t[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int i = static_cast<int>(threadIdx.x) + s * NT;
+        const int ic = i < n ? i : n - 1;
+        v[s] = val[ic];
+        t[s] = pos[ic];
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int i = static_cast<int>(threadIdx.x) + s * NT;
+        if (i < n) {
+          sm.c.ckey[off + i] = __float_as_uint(v[s]);
+          sm.c.cidx[off + i] = t[s];
+        }
+      }
+      off += n;
+    }
+  }
+  __syncthreads();
+  select_candidates<NT>(L, k, total, out, sm);
 }
 
 }  // namespace idx

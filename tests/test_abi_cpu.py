@@ -181,11 +181,15 @@ def test_workspace_sizes(lib):
         assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, k) == 0
         assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(r), 64, k) == 0
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r), 0, 4096) == 256
-    # long rows in a small batch: chunk candidates (2 x rows x chunks x k 4-byte values)
+    # long rows in a small batch: chunk candidates (2 x rows x chunks x 4096
+    # 4-byte values and a count per chunk for k <= 2048; k values per chunk
+    # above)
     rl = _rows(num_req=64, max_seq_len=131072, bt_width=2048, bt_stride=2048)
-    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 2048) == 256 + 2 * 4 * 64 * 4 * 2048
+    split = 2 * 4 * 64 * 4 * 4096 + 4 * 64 * 4
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 2048) == 256 + split
     assert lib.idx_workspace_bytes(B.IDX_OP_DECODE_TOPK, ctypes.byref(c), ctypes.byref(rl), 64, 2048) == \
-        256 + 64 * 131072 * 4 + 2 * 4 * 64 * 4 * 2048
+        256 + 64 * 131072 * 4 + split
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rl), 0, 3000) == 256 + 2 * 4 * 64 * 4 * 3000
     # many rows take the one-workgroup-per-row streaming path: no candidates
     rm = _rows(num_req=600, max_seq_len=131072, bt_width=2048)
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(rm), 0, 2048) == 256
@@ -197,7 +201,8 @@ def test_workspace_sizes(lib):
     r64x2 = _rows(num_req=64, next_n=2, max_seq_len=131072, bt_width=2048, bt_stride=2048)
     assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r64x2), 0, 2048) == 256
     r128 = _rows(num_req=128, max_seq_len=65536, bt_width=1024, bt_stride=1024)
-    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r128), 0, 2048) == 256 + 2 * 4 * 128 * 2 * 2048
+    assert lib.idx_workspace_bytes(B.IDX_OP_TOPK, None, ctypes.byref(r128), 0, 2048) == \
+        256 + 2 * 4 * 128 * 2 * 4096 + 4 * 128 * 2
     assert lib.idx_num_rows(ctypes.byref(_rows(num_req=3, next_n=2))) == 6
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=9))) == 5
     assert lib.idx_num_rows(ctypes.byref(_rows(kind=1, q_begin=4, q_end=3))) == -1

@@ -14,8 +14,12 @@ three levels with signed zeros (heavy ties in the threshold bin), the top
 keys crowded at one end of the row, and plain random rows.  Both selector
 kernels are covered: one 1024-thread workgroup per row (80 rows whose
 split would take more than 256 workgroups) and the 512-thread
-streaming-only kernel (512 rows).  Every output row carries a slack row
-after it that must stay untouched.
+streaming-only kernel (512 rows); and a batch small enough that its long
+rows are split over workgroups that share the sample threshold, each
+collecting one 32768-key chunk, with one workgroup per row selecting among
+the chunks' candidates (or from the whole row when the chunks together hold
+too few or too many).  Every output row carries a slack row after it that
+must stay untouched.
 """
 
 import numpy as np
@@ -105,5 +109,14 @@ def test_one_read_selection_lean_kernel(k):
     rng = np.random.default_rng(6000 + k)
     lens = [int(x) for x in rng.integers(16384, 65537, size=504)] + [16384, 16385, 32768, 32769, 65535,
                                                                       65536, 20000, 50001]
+    vals = [_pattern(i % 8, L, k, rng) for i, L in enumerate(lens)]
+    _run(lens, vals, k)
+
+
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_one_read_selection_split_rows(k):
+    rng = np.random.default_rng(7000 + k)
+    lens = [32769, 65536, 98304, 131072, 40000, 131071, 70001, 100000, 5000, 32768, 2 * k + 9, 65537, 120000,
+            90001, 33000, 131072]
     vals = [_pattern(i % 8, L, k, rng) for i, L in enumerate(lens)]
     _run(lens, vals, k)
