@@ -49,6 +49,10 @@ CASES = [
     # a chunk of fewer than 512 rows with rows past 32768 keys: the selector
     # splits those rows over workgroups and merges them
     ([40000, 300], [64, 16], 41000, 1 << 26, "fp8", 16, 64, 256),
+    # the same with the long rows' logits at an odd column offset (their
+    # keys start after the short request's 301), so the split reads rows
+    # that are not 16-byte aligned
+    ([301, 40000], [16, 64], 41000, 1 << 26, "fp8", 16, 64, 256),
 ]
 
 
