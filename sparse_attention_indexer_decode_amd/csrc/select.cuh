@@ -147,13 +147,11 @@ __device__ __forceinline__ void load_quads(const float* __restrict__ row, int ba
   }
 }
 
-// Loads in the form of load_quads, for contiguous per-lane keys: `whole`
-// (the same on every lane) says every lane's keys lie in the row and the
-// row is 16-byte aligned; otherwise each key is loaded from a clamped
-// position (L >= 1), one quad at a time, and the keys past L are flagged.
-
-// Loads keys [i0, i0 + 4*V) of a row into registers, all V loads in flight
-// together.
+// Loads keys [i0, i0 + 4*V) of a row into registers (contiguous per lane),
+// all V loads in flight together: `whole` (the same on every lane) says
+// that every lane's keys lie in the row and the row is 16-byte aligned;
+// otherwise each key is loaded from a clamped position (L >= 1), one quad
+// at a time, and the keys past L are flagged.
 template <int V>
 __device__ __forceinline__ void load_keys(const float* __restrict__ row, int i0, int L, bool whole,
                                           uint32_t (&u)[4 * V], bool (&v)[4 * V]) {
