@@ -214,13 +214,26 @@ __global__ __launch_bounds__(NT) void topk_split_merge_kernel(TopkParams p) {
   __shared__ int info[2];
   __shared__ int cnt[kMaxTopkChunks];
   const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t slot0 = static_cast<int64_t>(r) * p.chunks;
+  // requested with the row's length, in one round trip: the slots' counts
+  // and candidate tid of every slot (all of a slot of at most NT)
+  const int cnt_mine = tid < p.chunks ? p.cand_cnt[slot0 + tid] : 0;
+  float v0[kMaxTopkChunks];
+  int t0[kMaxTopkChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxTopkChunks; ++c) {
+    if (c < p.chunks) {
+      v0[c] = p.cand_val[(slot0 + c) * p.cap + tid];
+      t0[c] = p.cand_pos[(slot0 + c) * p.cap + tid];
+    }
+  }
   int L, col0;
   row_window<NT>(p.rows, r, L, col0, sm.scan, info);
   if (L <= kRowCap) return;  // finished by its chunk
   const int k = p.k;
   const int nc = (L + kRowCap - 1) / kRowCap;
-  const int64_t slot0 = static_cast<int64_t>(r) * p.chunks;
-  if (static_cast<int>(threadIdx.x) < nc) cnt[threadIdx.x] = p.cand_cnt[slot0 + threadIdx.x];
+  if (tid < nc) cnt[tid] = cnt_mine;
   __syncthreads();
   int total = 0;
   bool ok = true;
@@ -235,30 +248,37 @@ __global__ __launch_bounds__(NT) void topk_split_merge_kernel(TopkParams p) {
     return;
   }
   // the chunks' candidates, one after another, into the candidate area;
-  // every lane's loads in flight together (lanes past a chunk's count load
-  // its last candidate again and store nothing)
+  // past a slot's first NT, every lane's loads in flight together (lanes
+  // past the count load its last candidate again and store nothing)
   int off = 0;
-  for (int c = 0; c < nc; ++c) {
-    const int n = cnt[c];
-    if (n > 0) {
-      const float* val = p.cand_val + (slot0 + c) * p.cap;
-      const int32_t* pos = p.cand_pos + (slot0 + c) * p.cap;
-      constexpr int S = (kCandCap + NT - 1) / NT;
-      float v[S];
-      int t[S];
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int i = static_cast<int>(threadIdx.x) + s * NT;
-        const int ic = i < n ? i : n - 1;
-        v[s] = val[ic];
-        t[s] = pos[ic];
+  for (int c = 0; c < kMaxTopkChunks; ++c) {
+    if (c < nc) {
+      const int n = cnt[c];
+      if (tid < n) {
+        sm.c.ckey[off + tid] = __float_as_uint(v0[c]);
+        sm.c.cidx[off + tid] = t0[c];
       }
+      if (n > NT) {
+        const float* val = p.cand_val + (slot0 + c) * p.cap;
+        const int32_t* pos = p.cand_pos + (slot0 + c) * p.cap;
+        constexpr int S = (kCandCap + NT - 1) / NT;
+        float v[S];
+        int t[S];
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int i = static_cast<int>(threadIdx.x) + s * NT;
-        if (i < n) {
-          sm.c.ckey[off + i] = __float_as_uint(v[s]);
-          sm.c.cidx[off + i] = t[s];
+        for (int s = 1; s < S; ++s) {
+          const int i = tid + s * NT;
+          const int ic = i < n ? i : n - 1;
+          v[s] = val[ic];
+          t[s] = pos[ic];
+        }
+#pragma unroll
+        for (int s = 1; s < S; ++s) {
+          const int i = tid + s * NT;
+          if (i < n) {
+            sm.c.ckey[off + i] = __float_as_uint(v[s]);
+            sm.c.cidx[off + i] = t[s];
+          }
         }
       }
       off += n;
