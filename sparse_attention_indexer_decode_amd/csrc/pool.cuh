@@ -130,20 +130,32 @@ __global__ __launch_bounds__(NT) void pool_topk_kernel(PoolParams p) {
     const int gpw = kWave / lpp;             // pools per wave and step
     const int g = lane / lpp;
     const int sub = lane - g * lpp;
-    for (int c0 = wave * gpw; c0 < n; c0 += (NT / kWave) * gpw) {  // wave-uniform trip count
-      const int c = c0 + g;
-      float m = -INFINITY;
-      if (c < n) {
-        const float* src = row + (static_cast<int64_t>(a + c) << lg) + 4 * sub;
+    // kBatch steps' loads in flight together; lanes past the last pool load
+    // it again (no load under a lane-dependent branch, which would cost a
+    // round trip per load) and store nothing
+    constexpr int kBatch = 8;
+    const int step = (NT / kWave) * gpw;
+    for (int c0 = wave * gpw; c0 < n; c0 += kBatch * step) {  // wave-uniform trip count
+      float v[kBatch][4];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int c = c0 + t * step + g;
+        const float* src = row + (static_cast<int64_t>(a + (c < n ? c : n - 1)) << lg) + 4 * sub;
         if (aligned) {
           const float4 x = *reinterpret_cast<const float4*>(src);
-          m = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+          v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
         } else {
-          m = fmaxf(fmaxf(src[0], src[1]), fmaxf(src[2], src[3]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[t][e] = src[e];
         }
       }
-      for (int d = lpp >> 1; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-      if (c < n && sub == 0) sm.key[c] = ordered_key(m);
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int c = c0 + t * step + g;
+        float m = fmaxf(fmaxf(v[t][0], v[t][1]), fmaxf(v[t][2], v[t][3]));
+        for (int d = lpp >> 1; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+        if (c < n && sub == 0) sm.key[c] = ordered_key(m);
+      }
     }
     __syncthreads();
 
