@@ -327,11 +327,6 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(i > 0 ? i : 0);
 }
 
-// 2^(e - 127) as an fp32 (e = 0 is the subnormal 2^-127, e = 255 is NaN).
-__device__ __forceinline__ float ue8m0_to_float(uint32_t e) {
-  return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23));
-}
-
 // K-step s of one key's B fragment (this lane's 8 dims of the step) decoded
 // to bf16: fp8 codes exactly, or e2m1 values times their MX block scale.
 template <int D, bool MX>
@@ -339,8 +334,12 @@ __device__ __forceinline__ v8bf key_step(const uint8_t* rowp, int g, int s) {
   if (MX) {
     // D = 128: packed bytes [32 g, 32 g + 32) = blocks 2g, 2g+1 (dims 64 g ..)
     const uint32_t x = reinterpret_cast<const uint32_t*>(rowp + 32 * g)[s];
+    // The scaled conversion takes its power-of-two scale from the fp32
+    // exponent field alone (sign and mantissa ignored; byte 0 gives the
+    // 2^-127 of the MX format, byte 255 NaN), so each ue8m0 byte of the pair
+    // only has to be shifted into bits 23..30: one instruction per scale.
     const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rowp + D / 2 + 2 * g);
-    const float f = ue8m0_to_float(s < 4 ? (sc2 & 0xFFu) : (sc2 >> 8));
+    const float f = __uint_as_float(s < 4 ? sc2 << 23 : sc2 << 15);
     const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 0)),
                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 1)),
                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, f, 2)),

@@ -103,3 +103,48 @@ def test_contraction_precision_three_forms():
     assert ratios["fp8 1-term"] > 1.0
     # measured on MI355X: 3.9 (560 of 524288 keys outside the tolerance)
     assert ratios["fp8 2-term"] > 1.0
+
+
+MX_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "precision", "libmx_scale_probe.so")
+
+
+def test_mx_scale_operand_reads_the_exponent_field_only():
+    """The MXFP4 key decode hands the scaled fp4 -> bf16 conversion a 16-bit
+    pair of ue8m0 block-scale bytes shifted left by 23 (low byte in the fp32
+    exponent field, a bit of the high byte in the sign) or by 15 (high byte
+    in the exponent field, low byte in the mantissa), relying on the
+    instruction taking its power-of-two scale from the exponent field alone.
+    The test-only probe (tests/precision/mx_scale_probe.hip) converts all 16
+    e2m1 codes under every exponent byte in both positions, next to every
+    other byte in the other position; every bf16 must be the OCP MX value
+    code * 2^(e - 127) (exact: at most two significant bits, bf16 subnormals
+    included, values of 2^128 and more overflow to +-inf) and NaN for the
+    reserved byte 255."""
+    lib = ctypes.CDLL(MX_LIB)
+    lib.probe_mx_scale.restype = ctypes.c_int
+    lib.probe_mx_scale.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    e = np.arange(256, dtype=np.uint16)
+    # every (low, high) byte pair: each byte in turn holds every exponent
+    words = (e[:, None] | (e[None, :] << 8)).reshape(-1).astype(np.uint16)
+    n = len(words)
+    d = torch.device("cuda")
+    wd = torch.from_numpy(words.view(np.int16)).to(d)
+    out = torch.zeros((n, 16), dtype=torch.int32, device=d)
+    st = lib.probe_mx_scale(wd.data_ptr(), out.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, f"probe_mx_scale returned {st}"
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(n, 2, 2, 4)
+    # bf16 halves: nibble 2 s of code word c in the low half, 2 s + 1 in the high
+    halves = np.stack([got & 0xFFFF, got >> 16], axis=-1).astype(np.uint16)  # [n, form, c, s, half]
+    nib = (np.arange(2)[:, None, None] * 8 + np.arange(4)[None, :, None] * 2 + np.arange(2)[None, None, :])
+    val = oracle.formats.e2m1(nib)                                  # [c, s, half]
+    exps = np.stack([words & 0xFF, words >> 8], axis=1)             # [n, form]
+    scale = oracle.formats.ue8m0(exps.astype(np.uint8))             # [n, form]
+    exp = val[None, None] * scale[:, :, None, None, None]
+    exp = np.where(np.abs(exp) >= 2.0 ** 128, np.copysign(np.inf, exp), exp)
+    hw = oracle.formats.bf16(halves)
+    nan_ok = np.isnan(exp) == np.isnan(hw)
+    assert nan_ok.all(), "NaN where the scale byte is not 255, or a finite value where it is"
+    fin = ~np.isnan(exp)
+    same = (hw[fin] == exp[fin]) & (np.signbit(hw[fin]) == np.signbit(exp[fin]))
+    assert same.all(), f"{(~same).sum()} converted values differ from code * 2^(e - 127)"
